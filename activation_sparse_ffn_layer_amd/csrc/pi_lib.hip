@@ -1,0 +1,757 @@
+// Host side of libpi.so: context and scratch, argument checks, kernel selection, stack
+// runner with HIP graphs. See include/pi.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pi.h"
+#include "pi_kernels.hpp"
+
+using namespace pi;
+
+struct pi_ctx {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  int max_batch = 0, max_d = 0, max_ffn = 0, max_rank = 0;
+  int cus = 256;
+  size_t lds_max = 65536;
+  uint8_t* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* z = nullptr;           // [max_batch][max_rank]
+  uint64_t* mtok = nullptr;     // [max_batch][max_ffn/64]
+  uint64_t* munion = nullptr;   // [max_ffn/64]
+  int32_t* idx = nullptr;       // [max_ffn]
+  int32_t* nbuf = nullptr;      // [16]
+  float* a = nullptr;           // [max_batch][max_ffn]
+  float* part = nullptr;        // [G_MAX][max_batch][max_d]
+  float* y = nullptr;           // [max_batch][max_d]
+  uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
+  uint8_t* xstage = nullptr;    // [max_batch][max_d] fp32-sized
+  int32_t* nlog = nullptr;      // [NLOG_CAP]
+  std::string err;
+  // cached graph of one stack step, captured on a private stream (the caller's stream may be
+  // the null stream, which cannot be captured) and launched on the caller's stream
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  std::vector<const pi_ffn*> g_layers;
+  int g_B = 0;
+  // per-kernel event timing (pi_stack_profile only)
+  bool profiling = false;
+  std::vector<hipEvent_t> ev;     // pairs: ev[2i] before, ev[2i+1] after launch i
+  std::vector<int> ev_class;
+  size_t ev_used = 0;
+};
+
+struct pi_ffn {
+  pi_ffn_desc desc;
+  pi_ctx* ctx;
+};
+
+namespace {
+
+constexpr int G_MAX = 64;
+constexpr int NLOG_CAP = 4096;
+
+pi_status fail(pi_ctx* ctx, pi_status s, const char* fmt, ...) {
+  if (ctx != nullptr) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    ctx->err = buf;
+  }
+  return s;
+}
+
+#define PI_HIP(ctx, call)                                                                        \
+  do {                                                                                           \
+    hipError_t e_ = (call);                                                                      \
+    if (e_ != hipSuccess) return fail((ctx), PI_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Records a hipEvent pair around one kernel launch when the context is profiling.
+struct ProfScope {
+  pi_ctx* c;
+  size_t slot;
+  ProfScope(pi_ctx* ctx, int klass) : c(ctx), slot(SIZE_MAX) {
+    if (!c->profiling) return;
+    if (c->ev_used * 2 + 2 > c->ev.size()) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+      c->ev.push_back(a);
+      c->ev.push_back(b);
+      c->ev_class.push_back(klass);
+    }
+    slot = c->ev_used++;
+    c->ev_class[slot] = klass;
+    (void)hipEventRecord(c->ev[2 * slot], c->stream);
+  }
+  ~ProfScope() {
+    if (slot != SIZE_MAX) (void)hipEventRecord(c->ev[2 * slot + 1], c->stream);
+  }
+};
+enum { K_STAGE1 = 0, K_STAGE2, K_TRUEMASK, K_UP, K_DOWN, K_REDUCE, K_COUNT };
+static_assert(K_COUNT == PI_KERNEL_CLASSES, "kernel classes out of sync with pi.h");
+
+LayerDev to_dev(const pi_ffn_desc& d) {
+  LayerDev L;
+  L.d = d.d;
+  L.ffn = d.ffn;
+  L.rank = d.rank;
+  L.act = d.act;
+  L.wtype = d.wtype;
+  L.threshold = d.threshold;
+  L.w_up = static_cast<const uint8_t*>(d.w_up);
+  L.w_gate = static_cast<const uint8_t*>(d.w_gate);
+  L.w_down_t = static_cast<const uint8_t*>(d.w_down_t);
+  L.s_up = d.s_up;
+  L.s_gate = d.s_gate;
+  L.s_down = d.s_down;
+  L.b = d.b;
+  L.p_w1 = d.p_w1;
+  L.p_w2 = d.p_w2;
+  L.p_b = d.p_b;
+  return L;
+}
+
+int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+size_t x_elem(int wtype) { return wtype == PI_W_F32 ? 4 : 2; }
+
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+// ---------------------------------------------------------------- kernel dispatch tables
+
+template <int NB>
+pi_status launch_stage1_nb(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
+  const size_t budget = 65536;
+  int dc = (int)std::min<size_t>((size_t)L.d, budget / (NB * 2));
+  dc = dc / 512 * 512;
+  if (dc <= 0) dc = L.d;
+  if (dc > L.d) dc = L.d;
+  const size_t lds = (size_t)NB * dc * 2;
+  PI_HIP(c, allow_lds(k_stage1<NB>, lds));
+  const int grid = (L.rank + NWAVES - 1) / NWAVES;
+  ProfScope ps(c, K_STAGE1);
+  hipLaunchKernelGGL(k_stage1<NB>, dim3(grid), dim3(BLOCK), lds, c->stream, L, xin, B, dc, c->z);
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+pi_status launch_stage1(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
+  switch (nb_for(B)) {
+    case 1: return launch_stage1_nb<1>(c, L, xin, B);
+    case 2: return launch_stage1_nb<2>(c, L, xin, B);
+    case 4: return launch_stage1_nb<4>(c, L, xin, B);
+    default: return launch_stage1_nb<8>(c, L, xin, B);
+  }
+}
+
+template <int NB, int CPL>
+pi_status launch_stage2_t(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits) {
+  constexpr int RPW = NB == 1 ? 16 : NB == 2 ? 8 : NB == 4 ? 4 : 2;
+  ProfScope ps(c, K_STAGE2);
+  hipLaunchKernelGGL((k_stage2<NB, CPL, RPW>), dim3(L.ffn / 64), dim3(BLOCK), 0, c->stream, L, c->z, B, mtok,
+                     c->munion, logits);
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+template <int NB>
+pi_status launch_stage2_nb(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits) {
+  const int cpl = (L.rank + 511) / 512;
+  if (cpl <= 1) return launch_stage2_t<NB, 1>(c, L, B, mtok, logits);
+  if (cpl <= 2) return launch_stage2_t<NB, 2>(c, L, B, mtok, logits);
+  return launch_stage2_t<NB, 4>(c, L, B, mtok, logits);
+}
+
+pi_status launch_stage2(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits) {
+  switch (nb_for(B)) {
+    case 1: return launch_stage2_nb<1>(c, L, B, mtok, logits);
+    case 2: return launch_stage2_nb<2>(c, L, B, mtok, logits);
+    case 4: return launch_stage2_nb<4>(c, L, B, mtok, logits);
+    default: return launch_stage2_nb<8>(c, L, B, mtok, logits);
+  }
+}
+
+template <int WT, int NB>
+pi_status launch_truemask_t(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
+  constexpr bool XF32 = WT == W_F32;
+  const size_t lds = (size_t)NB * L.d * (XF32 ? 4 : 2);
+  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
+  PI_HIP(c, allow_lds(k_truemask<WT, NB, XF32>, lds));
+  ProfScope ps(c, K_TRUEMASK);
+  hipLaunchKernelGGL((k_truemask<WT, NB, XF32>), dim3(L.ffn / 64), dim3(BLOCK), lds, c->stream, L, xin, B, mtok,
+                     c->munion, logits);
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+template <int WT>
+pi_status launch_truemask_w(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
+  switch (nb_for(B)) {
+    case 1: return launch_truemask_t<WT, 1>(c, L, xin, B, mtok, logits);
+    case 2: return launch_truemask_t<WT, 2>(c, L, xin, B, mtok, logits);
+    case 4: return launch_truemask_t<WT, 4>(c, L, xin, B, mtok, logits);
+    default: return launch_truemask_t<WT, 8>(c, L, xin, B, mtok, logits);
+  }
+}
+
+pi_status launch_truemask(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
+  switch (L.wtype) {
+    case W_F32: return launch_truemask_w<W_F32>(c, L, xin, B, mtok, logits);
+    case W_F16: return launch_truemask_w<W_F16>(c, L, xin, B, mtok, logits);
+    default: return launch_truemask_w<W_Q4>(c, L, xin, B, mtok, logits);
+  }
+}
+
+int up_grid(const pi_ctx* c, const LayerDev& L) {
+  return std::max(1, std::min((L.ffn + NWAVES - 1) / NWAVES, 2 * c->cus));
+}
+
+template <int WT, int ACT, int NB, bool SCAN>
+pi_status launch_up_t(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in,
+                      const int32_t* n_in, int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+  const size_t xe = (WT == W_F32) ? 4 : 2;
+  const int W = L.ffn / 64;
+  const size_t lds = (size_t)NB * L.d * xe + (SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
+  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
+  PI_HIP(c, allow_lds(k_up<WT, ACT, NB, SCAN>, lds));
+  ProfScope ps(c, K_UP);
+  hipLaunchKernelGGL((k_up<WT, ACT, NB, SCAN>), dim3(up_grid(c, L)), dim3(BLOCK), lds, c->stream, L, x, B, c->munion,
+                     idx_in, n_in, idx_out, n_out, n_log, c->a);
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+template <int WT, int ACT, bool SCAN>
+pi_status launch_up_a(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in,
+                      int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+  switch (nb_for(B)) {
+    case 1: return launch_up_t<WT, ACT, 1, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    case 2: return launch_up_t<WT, ACT, 2, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    case 4: return launch_up_t<WT, ACT, 4, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    default: return launch_up_t<WT, ACT, 8, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+  }
+}
+
+template <bool SCAN>
+pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in,
+                    int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+  if (L.act == ACT_RELU) {
+    switch (L.wtype) {
+      case W_F32: return launch_up_a<W_F32, ACT_RELU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+      case W_F16: return launch_up_a<W_F16, ACT_RELU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+      default: return launch_up_a<W_Q4, ACT_RELU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    }
+  }
+  switch (L.wtype) {
+    case W_F32: return launch_up_a<W_F32, ACT_REGLU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    case W_F16: return launch_up_a<W_F16, ACT_REGLU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    default: return launch_up_a<W_Q4, ACT_REGLU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+  }
+}
+
+int slice_width(int wtype) {
+  return wtype == W_F16 ? DownGeom<W_F16>::SW : wtype == W_F32 ? DownGeom<W_F32>::SW : DownGeom<W_Q4>::SW;
+}
+
+int down_groups(const LayerDev& L) {
+  const int S = (L.d + slice_width(L.wtype) - 1) / slice_width(L.wtype);
+  return std::max(8, std::min(G_MAX, 1024 / S));
+}
+
+template <int WT, int NB>
+pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx, const int32_t* n, int G) {
+  const int S = (L.d + DownGeom<WT>::SW - 1) / DownGeom<WT>::SW;
+  ProfScope ps(c, K_DOWN);
+  hipLaunchKernelGGL((k_down<WT, NB>), dim3(G, S), dim3(BLOCK), 0, c->stream, L, B, idx, n, c->a, c->part, G);
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+template <int WT>
+pi_status launch_down_w(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx, const int32_t* n, int G) {
+  switch (nb_for(B)) {
+    case 1: return launch_down_t<WT, 1>(c, L, B, idx, n, G);
+    case 2: return launch_down_t<WT, 2>(c, L, B, idx, n, G);
+    case 4: if constexpr (WT != W_Q4) return launch_down_t<WT, 4>(c, L, B, idx, n, G); break;
+    default: if constexpr (WT != W_Q4) return launch_down_t<WT, 8>(c, L, B, idx, n, G); break;
+  }
+  return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 down projection supports batch <= 2 on this path");
+}
+
+pi_status launch_down_reduce(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx, const int32_t* n, float* y) {
+  const int G = down_groups(L);
+  pi_status s;
+  switch (L.wtype) {
+    case W_F32: s = launch_down_w<W_F32>(c, L, B, idx, n, G); break;
+    case W_F16: s = launch_down_w<W_F16>(c, L, B, idx, n, G); break;
+    default: s = launch_down_w<W_Q4>(c, L, B, idx, n, G); break;
+  }
+  if (s != PI_OK) return s;
+  const int BD = B * L.d;
+  {
+    ProfScope ps(c, K_REDUCE);
+    hipLaunchKernelGGL(k_reduce, dim3((BD + WAVE - 1) / WAVE), dim3(BLOCK), 0, c->stream, c->part, G, BD, y);
+  }
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+pi_status launch_compact(pi_ctx* c, int ffn, int32_t* idx, int32_t* n) {
+  const int W = ffn / 64;
+  hipLaunchKernelGGL(k_compact, dim3((W + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, c->stream, c->munion, W, idx, n,
+                     (int32_t*)nullptr);
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+// ---------------------------------------------------------------- argument checks
+
+pi_status check_batch(pi_ctx* c, const pi_ffn_desc& d, int B) {
+  if (B < 1) return fail(c, PI_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  if (B > c->max_batch) return fail(c, PI_ERR_INVALID, "B %d exceeds the context's max_batch %d", B, c->max_batch);
+  if (B > 8) return fail(c, PI_ERR_UNSUPPORTED, "batch %d: this build runs batches of 1..8 tokens", B);
+  if (d.wtype == PI_W_Q4_0 && B > 2)
+    return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
+  return PI_OK;
+}
+
+pi_status check_dev_ptr(pi_ctx* c, const void* p, const char* name, bool nullable = false) {
+  if (p == nullptr) return nullable ? PI_OK : fail(c, PI_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(p)) return fail(c, PI_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return PI_OK;
+}
+
+#define PI_TRY(expr)                 \
+  do {                               \
+    pi_status s_ = (expr);           \
+    if (s_ != PI_OK) return s_;      \
+  } while (0)
+
+// Enqueue the whole layer for one batch. xin: where x comes from; x_cur: the layer's input
+// in global memory as the up kernel reads it (equal to xin.x, or xin.x_out in glue mode).
+pi_status enqueue_layer(pi_ctx* c, const pi_ffn* f, const XIn& xin, const void* x_cur, int B, float* y,
+                        uint64_t* mask, int32_t* idx, int32_t* n, int32_t* n_log) {
+  const LayerDev L = to_dev(f->desc);
+  if (L.rank > 0) {
+    PI_TRY(launch_stage1(c, L, xin, B));
+    PI_TRY(launch_stage2(c, L, B, mask, nullptr));
+  } else {
+    PI_TRY(launch_truemask(c, L, xin, B, mask, nullptr));
+  }
+  PI_TRY(launch_up<true>(c, L, x_cur, B, nullptr, nullptr, idx, n, n_log));
+  PI_TRY(launch_down_reduce(c, L, B, idx, n, y));
+  return PI_OK;
+}
+
+}  // namespace
+
+// ======================================================================== exported ABI
+
+extern "C" {
+
+int32_t pi_abi_version(void) { return PI_ABI_VERSION; }
+
+const char* pi_status_str(pi_status s) {
+  switch (s) {
+    case PI_OK: return "ok";
+    case PI_ERR_INVALID: return "invalid argument";
+    case PI_ERR_UNSUPPORTED: return "unsupported";
+    case PI_ERR_OOM: return "out of device memory";
+    case PI_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pi_last_error(const pi_ctx* ctx) { return ctx == nullptr ? "" : ctx->err.c_str(); }
+
+pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int32_t max_d, int32_t max_ffn,
+                        int32_t max_rank, pi_ctx** out) {
+  if (out == nullptr) return PI_ERR_INVALID;
+  *out = nullptr;
+  if (max_batch < 1 || max_d < 8 || max_ffn < 64 || max_rank < 0 || max_d % 8 || max_ffn % 64)
+    return PI_ERR_INVALID;
+  pi_ctx* c = new (std::nothrow) pi_ctx();
+  if (c == nullptr) return PI_ERR_OOM;
+  c->device = device;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  c->max_batch = max_batch;
+  c->max_d = max_d;
+  c->max_ffn = max_ffn;
+  c->max_rank = max_rank;
+  if (hipSetDevice(device) != hipSuccess) {
+    delete c;
+    return PI_ERR_HIP;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) == hipSuccess) {
+    c->cus = prop.multiProcessorCount;
+    c->lds_max = prop.sharedMemPerBlock;
+  }
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t B = max_batch, D = max_d, F = max_ffn, R = std::max(max_rank, 8);
+  size_t off = 0;
+  const size_t o_z = off; off += al(B * R * 4);
+  const size_t o_mt = off; off += al(B * (F / 64) * 8);
+  const size_t o_mu = off; off += al((F / 64) * 8);
+  const size_t o_idx = off; off += al(F * 4);
+  const size_t o_n = off; off += al(16 * 4);
+  const size_t o_a = off; off += al(B * F * 4);
+  const size_t o_part = off; off += al((size_t)G_MAX * B * D * 4);
+  const size_t o_y = off; off += al(B * D * 4);
+  const size_t o_x0 = off; off += al(B * D * 4);
+  const size_t o_x1 = off; off += al(B * D * 4);
+  const size_t o_xs = off; off += al(B * D * 4);
+  const size_t o_nlog = off; off += al(NLOG_CAP * 4);
+  if (hipMalloc(reinterpret_cast<void**>(&c->ws), off) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return PI_ERR_OOM;
+  }
+  c->ws_bytes = off;
+  if (hipMemset(c->ws, 0, off) != hipSuccess) {
+    (void)hipFree(c->ws);
+    delete c;
+    return PI_ERR_HIP;
+  }
+  c->z = reinterpret_cast<float*>(c->ws + o_z);
+  c->mtok = reinterpret_cast<uint64_t*>(c->ws + o_mt);
+  c->munion = reinterpret_cast<uint64_t*>(c->ws + o_mu);
+  c->idx = reinterpret_cast<int32_t*>(c->ws + o_idx);
+  c->nbuf = reinterpret_cast<int32_t*>(c->ws + o_n);
+  c->a = reinterpret_cast<float*>(c->ws + o_a);
+  c->part = reinterpret_cast<float*>(c->ws + o_part);
+  c->y = reinterpret_cast<float*>(c->ws + o_y);
+  c->xbuf[0] = c->ws + o_x0;
+  c->xbuf[1] = c->ws + o_x1;
+  c->xstage = c->ws + o_xs;
+  c->nlog = reinterpret_cast<int32_t*>(c->ws + o_nlog);
+  if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) {
+    (void)hipFree(c->ws);
+    delete c;
+    return PI_ERR_HIP;
+  }
+  *out = c;
+  return PI_OK;
+}
+
+void pi_ctx_destroy(pi_ctx* ctx) {
+  if (ctx == nullptr) return;
+  (void)hipSetDevice(ctx->device);
+  if (ctx->gexec != nullptr) (void)hipGraphExecDestroy(ctx->gexec);
+  if (ctx->cap_stream != nullptr) (void)hipStreamDestroy(ctx->cap_stream);
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
+  if (ctx->ws != nullptr) (void)hipFree(ctx->ws);
+  delete ctx;
+}
+
+pi_status pi_ctx_set_stream(pi_ctx* ctx, void* hip_stream) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  ctx->stream = static_cast<hipStream_t>(hip_stream);
+  if (ctx->gexec != nullptr) {
+    (void)hipGraphExecDestroy(ctx->gexec);
+    ctx->gexec = nullptr;
+    ctx->g_layers.clear();
+  }
+  return PI_OK;
+}
+
+pi_status pi_ffn_create(pi_ctx* ctx, const pi_ffn_desc* desc, pi_ffn** out) {
+  if (ctx == nullptr || out == nullptr) return PI_ERR_INVALID;
+  *out = nullptr;
+  if (desc == nullptr) return fail(ctx, PI_ERR_INVALID, "desc is NULL");
+  const pi_ffn_desc& d = *desc;
+  if (d.d < 8 || d.d % 8) return fail(ctx, PI_ERR_INVALID, "d must be a positive multiple of 8 (got %d)", d.d);
+  if (d.ffn < 64 || d.ffn % 64) return fail(ctx, PI_ERR_INVALID, "ffn must be a positive multiple of 64 (got %d)", d.ffn);
+  if (d.rank < 0 || d.rank % 8) return fail(ctx, PI_ERR_INVALID, "rank must be 0 or a multiple of 8 (got %d)", d.rank);
+  if (d.rank > 2048) return fail(ctx, PI_ERR_UNSUPPORTED, "rank %d above 2048", d.rank);
+  if (d.d > ctx->max_d || d.ffn > ctx->max_ffn || d.rank > ctx->max_rank)
+    return fail(ctx, PI_ERR_INVALID, "layer %dx%d rank %d exceeds the context (%dx%d rank %d)", d.d, d.ffn, d.rank,
+                ctx->max_d, ctx->max_ffn, ctx->max_rank);
+  if (d.act != PI_ACT_RELU && d.act != PI_ACT_REGLU) return fail(ctx, PI_ERR_INVALID, "unknown activation %d", d.act);
+  if (d.wtype != PI_W_F32 && d.wtype != PI_W_F16 && d.wtype != PI_W_Q4_0)
+    return fail(ctx, PI_ERR_INVALID, "unknown weight type %d", d.wtype);
+  if (d.wtype == PI_W_Q4_0 && d.d % 32) return fail(ctx, PI_ERR_INVALID, "Q4_0 needs d %% 32 == 0 (got %d)", d.d);
+  if (d.wtype == PI_W_F32 && d.rank > 0)
+    return fail(ctx, PI_ERR_UNSUPPORTED, "the predictor runs on fp16 tokens: fp32 layers take rank 0");
+  PI_TRY(check_dev_ptr(ctx, d.w_up, "w_up"));
+  PI_TRY(check_dev_ptr(ctx, d.w_down_t, "w_down_t"));
+  PI_TRY(check_dev_ptr(ctx, d.b, "b"));
+  if (d.act == PI_ACT_REGLU) PI_TRY(check_dev_ptr(ctx, d.w_gate, "w_gate"));
+  if (d.wtype == PI_W_Q4_0) {
+    PI_TRY(check_dev_ptr(ctx, d.s_up, "s_up"));
+    PI_TRY(check_dev_ptr(ctx, d.s_down, "s_down"));
+    if (d.act == PI_ACT_REGLU) PI_TRY(check_dev_ptr(ctx, d.s_gate, "s_gate"));
+  }
+  if (d.rank > 0) {
+    PI_TRY(check_dev_ptr(ctx, d.p_w1, "p_w1"));
+    PI_TRY(check_dev_ptr(ctx, d.p_w2, "p_w2"));
+    PI_TRY(check_dev_ptr(ctx, d.p_b, "p_b"));
+  }
+  pi_ffn* f = new (std::nothrow) pi_ffn();
+  if (f == nullptr) return fail(ctx, PI_ERR_OOM, "host allocation failed");
+  f->desc = d;
+  f->ctx = ctx;
+  *out = f;
+  return PI_OK;
+}
+
+void pi_ffn_destroy(pi_ffn* ffn) { delete ffn; }
+
+pi_status pi_predict(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, uint64_t* mask, int32_t* idx,
+                     int32_t* n_active, float* logits_out) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (ffn == nullptr) return fail(ctx, PI_ERR_INVALID, "ffn is NULL");
+  PI_TRY(check_batch(ctx, ffn->desc, B));
+  PI_TRY(check_dev_ptr(ctx, x, "x"));
+  PI_TRY(check_dev_ptr(ctx, mask, "mask"));
+  PI_TRY(check_dev_ptr(ctx, idx, "idx"));
+  PI_TRY(check_dev_ptr(ctx, n_active, "n_active"));
+  PI_TRY(check_dev_ptr(ctx, logits_out, "logits_out", true));
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const LayerDev L = to_dev(ffn->desc);
+  const XIn xin{x, nullptr, nullptr};
+  if (L.rank > 0) {
+    PI_TRY(launch_stage1(ctx, L, xin, B));
+    PI_TRY(launch_stage2(ctx, L, B, mask, logits_out));
+  } else {
+    PI_TRY(launch_truemask(ctx, L, xin, B, mask, logits_out));
+  }
+  return launch_compact(ctx, L.ffn, idx, n_active);
+}
+
+pi_status pi_sparse_ffn(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, const int32_t* idx,
+                        const int32_t* n_active, float* y) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (ffn == nullptr) return fail(ctx, PI_ERR_INVALID, "ffn is NULL");
+  PI_TRY(check_batch(ctx, ffn->desc, B));
+  PI_TRY(check_dev_ptr(ctx, x, "x"));
+  PI_TRY(check_dev_ptr(ctx, idx, "idx"));
+  PI_TRY(check_dev_ptr(ctx, n_active, "n_active"));
+  PI_TRY(check_dev_ptr(ctx, y, "y"));
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const LayerDev L = to_dev(ffn->desc);
+  PI_TRY(launch_up<false>(ctx, L, x, B, idx, n_active, nullptr, nullptr, nullptr));
+  return launch_down_reduce(ctx, L, B, idx, n_active, y);
+}
+
+pi_status pi_layer(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, float* y, uint64_t* mask, int32_t* idx,
+                   int32_t* n_active) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (ffn == nullptr) return fail(ctx, PI_ERR_INVALID, "ffn is NULL");
+  PI_TRY(check_batch(ctx, ffn->desc, B));
+  PI_TRY(check_dev_ptr(ctx, x, "x"));
+  PI_TRY(check_dev_ptr(ctx, y, "y"));
+  PI_TRY(check_dev_ptr(ctx, mask, "mask", true));
+  PI_TRY(check_dev_ptr(ctx, idx, "idx", true));
+  PI_TRY(check_dev_ptr(ctx, n_active, "n_active", true));
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const XIn xin{x, nullptr, nullptr};
+  return enqueue_layer(ctx, ffn, xin, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
+}
+
+pi_status pi_compact(pi_ctx* ctx, const float* v, int32_t B, int32_t ffn, float threshold, uint64_t* mask,
+                     int32_t* idx, int32_t* n_active) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (B < 1 || B > ctx->max_batch) return fail(ctx, PI_ERR_INVALID, "B %d out of range 1..%d", B, ctx->max_batch);
+  if (B > 8) return fail(ctx, PI_ERR_UNSUPPORTED, "pi_compact handles batches of 1..8");
+  if (ffn < 64 || ffn % 64 || ffn > ctx->max_ffn)
+    return fail(ctx, PI_ERR_INVALID, "ffn must be a multiple of 64 up to %d (got %d)", ctx->max_ffn, ffn);
+  PI_TRY(check_dev_ptr(ctx, v, "v"));
+  PI_TRY(check_dev_ptr(ctx, mask, "mask"));
+  PI_TRY(check_dev_ptr(ctx, idx, "idx"));
+  PI_TRY(check_dev_ptr(ctx, n_active, "n_active"));
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const dim3 grid(ffn / 64);
+  switch (nb_for(B)) {
+    case 1: hipLaunchKernelGGL(k_threshold<1>, grid, dim3(WAVE), 0, ctx->stream, v, B, ffn, threshold, mask, ctx->munion); break;
+    case 2: hipLaunchKernelGGL(k_threshold<2>, grid, dim3(WAVE), 0, ctx->stream, v, B, ffn, threshold, mask, ctx->munion); break;
+    case 4: hipLaunchKernelGGL(k_threshold<4>, grid, dim3(WAVE), 0, ctx->stream, v, B, ffn, threshold, mask, ctx->munion); break;
+    default: hipLaunchKernelGGL(k_threshold<8>, grid, dim3(WAVE), 0, ctx->stream, v, B, ffn, threshold, mask, ctx->munion); break;
+  }
+  PI_HIP(ctx, hipGetLastError());
+  return launch_compact(ctx, ffn, idx, n_active);
+}
+
+pi_status pi_glue(pi_ctx* ctx, const float* y, const void* x_prev, int32_t B, int32_t d, int32_t x_is_f32,
+                  void* x_out) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (B < 1 || d < 8 || d % 8) return fail(ctx, PI_ERR_INVALID, "bad shape B=%d d=%d", B, d);
+  PI_TRY(check_dev_ptr(ctx, y, "y"));
+  PI_TRY(check_dev_ptr(ctx, x_prev, "x_prev"));
+  PI_TRY(check_dev_ptr(ctx, x_out, "x_out"));
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  if (x_is_f32) hipLaunchKernelGGL(k_glue<true>, dim3(B), dim3(BLOCK), 0, ctx->stream, y, x_prev, d, x_out);
+  else hipLaunchKernelGGL(k_glue<false>, dim3(B), dim3(BLOCK), 0, ctx->stream, y, x_prev, d, x_out);
+  PI_HIP(ctx, hipGetLastError());
+  return PI_OK;
+}
+
+pi_status pi_hot_first_order(const double* p, int32_t ffn, int32_t* perm) {
+  if (p == nullptr || perm == nullptr || ffn < 1) return PI_ERR_INVALID;
+  std::vector<int32_t> order(ffn);
+  for (int32_t i = 0; i < ffn; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [p](int32_t a, int32_t b) { return p[a] > p[b]; });
+  std::memcpy(perm, order.data(), sizeof(int32_t) * ffn);
+  return PI_OK;
+}
+
+pi_status pi_permute_rows(pi_ctx* ctx, const void* src, void* dst, const int32_t* perm, int32_t rows,
+                          int64_t row_bytes) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (rows < 1 || row_bytes < 4 || row_bytes % 4)
+    return fail(ctx, PI_ERR_INVALID, "rows %d / row_bytes %lld invalid", rows, (long long)row_bytes);
+  if (src == nullptr || dst == nullptr || perm == nullptr) return fail(ctx, PI_ERR_INVALID, "NULL pointer");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 3u)
+    return fail(ctx, PI_ERR_INVALID, "src/dst not 4-byte aligned");
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  const uint8_t* d = static_cast<const uint8_t*>(dst);
+  const size_t span = (size_t)rows * (size_t)row_bytes;
+  if (s < d + span && d < s + span) return fail(ctx, PI_ERR_INVALID, "src and dst overlap");
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const long long rb = row_bytes;
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) && (rb & 15) == 0)
+    return fail(ctx, PI_ERR_INVALID, "src/dst must be 16-byte aligned when row_bytes %% 16 == 0");
+  hipLaunchKernelGGL(k_permute_rows, dim3(rows), dim3(BLOCK), 0, ctx->stream, static_cast<const uint8_t*>(src),
+                     static_cast<uint8_t*>(dst), perm, (int)rows, rb);
+  PI_HIP(ctx, hipGetLastError());
+  return PI_OK;
+}
+
+static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens,
+                                   int32_t T, int32_t B, float* y_out, int32_t* n_active_log, int32_t use_graph) {
+  if (layers == nullptr || L < 1) return fail(ctx, PI_ERR_INVALID, "need at least one layer");
+  if (L > NLOG_CAP) return fail(ctx, PI_ERR_INVALID, "at most %d layers", NLOG_CAP);
+  if (T < 1 || B < 1 || T % B) return fail(ctx, PI_ERR_INVALID, "T %d must be a positive multiple of B %d", T, B);
+  for (int l = 0; l < L; ++l) {
+    if (layers[l] == nullptr) return fail(ctx, PI_ERR_INVALID, "layer %d is NULL", l);
+    if (layers[l]->ctx != ctx) return fail(ctx, PI_ERR_INVALID, "layer %d belongs to another context", l);
+    PI_TRY(check_batch(ctx, layers[l]->desc, B));
+    if (layers[l]->desc.d != layers[0]->desc.d || layers[l]->desc.wtype != layers[0]->desc.wtype)
+      return fail(ctx, PI_ERR_INVALID, "layer %d: all layers need the same d and weight type", l);
+  }
+  PI_TRY(check_dev_ptr(ctx, x_tokens, "x_tokens"));
+  PI_TRY(check_dev_ptr(ctx, y_out, "y_out"));
+  PI_TRY(check_dev_ptr(ctx, n_active_log, "n_active_log", true));
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const int d = layers[0]->desc.d;
+  const size_t xe = x_elem(layers[0]->desc.wtype);
+  const size_t xbytes = (size_t)B * d * xe, ybytes = (size_t)B * d * 4;
+
+  auto enqueue_step = [&]() -> pi_status {
+    for (int l = 0; l < L; ++l) {
+      XIn xin;
+      const void* x_cur;
+      if (l == 0) {
+        xin = XIn{ctx->xstage, nullptr, nullptr};
+        x_cur = ctx->xstage;
+      } else {
+        const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
+        xin = XIn{x_prev, ctx->y, ctx->xbuf[l & 1]};
+        x_cur = ctx->xbuf[l & 1];
+      }
+      PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, ctx->y, nullptr, ctx->idx, ctx->nbuf, ctx->nlog + l));
+    }
+    return PI_OK;
+  };
+
+  bool graph_ok = false;
+  if (use_graph) {
+    std::vector<const pi_ffn*> key(layers, layers + L);
+    if (ctx->gexec != nullptr && ctx->g_layers == key && ctx->g_B == B) {
+      graph_ok = true;
+    } else {
+      if (ctx->gexec != nullptr) {
+        (void)hipGraphExecDestroy(ctx->gexec);
+        ctx->gexec = nullptr;
+      }
+      hipStream_t user = ctx->stream;
+      ctx->stream = ctx->cap_stream;
+      hipError_t e = hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal);
+      if (e != hipSuccess) {
+        ctx->stream = user;
+        return fail(ctx, PI_ERR_HIP, "graph capture: %s", hipGetErrorString(e));
+      }
+      pi_status s = enqueue_step();
+      hipGraph_t graph = nullptr;
+      e = hipStreamEndCapture(ctx->cap_stream, &graph);
+      ctx->stream = user;
+      if (s != PI_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return s;
+      }
+      if (e != hipSuccess) return fail(ctx, PI_ERR_HIP, "graph capture: %s", hipGetErrorString(e));
+      e = hipGraphInstantiate(&ctx->gexec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (e != hipSuccess) {
+        ctx->gexec = nullptr;
+        return fail(ctx, PI_ERR_HIP, "graph instantiate: %s", hipGetErrorString(e));
+      }
+      ctx->g_layers = key;
+      ctx->g_B = B;
+      graph_ok = true;
+    }
+  }
+  const uint8_t* xt = static_cast<const uint8_t*>(x_tokens);
+  for (int s = 0; s < T / B; ++s) {
+    PI_HIP(ctx, hipMemcpyAsync(ctx->xstage, xt + (size_t)s * xbytes, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    if (graph_ok) {
+      PI_HIP(ctx, hipGraphLaunch(ctx->gexec, ctx->stream));
+    } else {
+      PI_TRY(enqueue_step());
+    }
+    PI_HIP(ctx, hipMemcpyAsync(reinterpret_cast<uint8_t*>(y_out) + (size_t)s * ybytes, ctx->y, ybytes,
+                               hipMemcpyDeviceToDevice, ctx->stream));
+    if (n_active_log != nullptr)
+      PI_HIP(ctx, hipMemcpyAsync(n_active_log + (size_t)s * L, ctx->nlog, (size_t)L * 4, hipMemcpyDeviceToDevice,
+                                 ctx->stream));
+  }
+  return PI_OK;
+}
+
+pi_status pi_stack_run(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens, int32_t T,
+                       int32_t B, float* y_out, int32_t* n_active_log, int32_t use_graph) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  return pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, use_graph);
+}
+
+pi_status pi_stack_profile(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens, int32_t T,
+                           int32_t B, float* y_out, int32_t* n_active_log, double* ms_out, int64_t* launches_out) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (ms_out == nullptr || launches_out == nullptr) return fail(ctx, PI_ERR_INVALID, "NULL output array");
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  ctx->profiling = true;
+  ctx->ev_used = 0;
+  pi_status s = pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, 0);
+  ctx->profiling = false;
+  if (s != PI_OK) return s;
+  PI_HIP(ctx, hipStreamSynchronize(ctx->stream));
+  for (int k = 0; k < PI_KERNEL_CLASSES; ++k) {
+    ms_out[k] = 0.0;
+    launches_out[k] = 0;
+  }
+  for (size_t i = 0; i < ctx->ev_used; ++i) {
+    float ms = 0.f;
+    PI_HIP(ctx, hipEventElapsedTime(&ms, ctx->ev[2 * i], ctx->ev[2 * i + 1]));
+    ms_out[ctx->ev_class[i]] += ms;
+    launches_out[ctx->ev_class[i]] += 1;
+  }
+  return PI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,246 @@
+#!/usr/bin/env python
+"""Sparse-FFN decode throughput on one MI355X.
+
+A step is one pass of the whole hot path over one batch: every layer of the stack runs the
+low-rank predictor, the threshold and compaction, the gathered up/gate rows with their
+activation and the scattered down columns, chained layer to layer by the rms glue. The
+default workload is the OPT-6.7B-shaped stack (32 ReLU layers, d=4096, ffn=16384, rank-1024
+fp16 predictor, fp16 weights) at batch 1, with seeded synthetic weights and tokens resident
+in HBM before timing starts.
+
+Prints one JSON line: tokens/s over the timed steps, a roofline entry for the kernel that
+takes the most time (algorithmic bytes per launch over its HIP-event-timed duration, against
+MI355X's 8 TB/s), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import dataclasses
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-FFN tokens/s at batch 1 (layer stack) + % of HBM peak on active bytes"
+HBM_PEAK_GBS = 8000.0
+WBYTES = {"f32": 4.0, "f16": 2.0, "q4_0": 18.0 / 32.0}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128, help="timed steps (tokens at batch 1)")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="opt6.7b")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=None, help="override the stack depth (exploration only)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--profile-steps", type=int, default=16, help="steps of the per-kernel event pass")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def build_stack(cfg, seed, pi, ctx):
+    """Generate every layer in device memory; hot-first workloads are permuted on the device."""
+    import torch
+    from synth import make_layer
+    layers, ffns, tables = [], [], []
+    for li in range(cfg.layers):
+        L = make_layer(cfg, li, master=seed, device="cuda")
+        table = None
+        if cfg.hot_first:
+            perm = torch.from_numpy(pi.hot_first_order(L.p)).cuda()
+
+            def pr(t):
+                if t is None:
+                    return None
+                out = torch.empty_like(t)
+                pi.permute_rows(ctx, t, out, perm)
+                return out
+            L = dataclasses.replace(L, w_up=pr(L.w_up), w_gate=pr(L.w_gate), w_down_t=pr(L.w_down_t),
+                                    s_up=pr(L.s_up), s_gate=pr(L.s_gate), s_down=pr(L.s_down), b=pr(L.b),
+                                    p_w2=pr(L.p_w2), p_b=pr(L.p_b), p=L.p[perm.cpu().numpy()])
+            table = perm
+        layers.append(L)
+        tables.append(table)
+        ffns.append(pi.Ffn(ctx, L, neuron_table=table))
+    torch.cuda.synchronize()
+    return layers, ffns
+
+
+def kernel_bytes(cls, L, B, n_list):
+    """Algorithmic bytes moved by the launches of one kernel class on one layer.
+
+    n_list: active (union) counts of the launches."""
+    w = WBYTES[L.wtype]
+    xe = 4 if L.wtype == "f32" else 2
+    d, F, r = L.d, L.ffn, L.rank
+    k_up = 1 if L.act == "relu" else 2
+    if cls == "stage1":
+        return len(n_list) * (r * d * 2 + B * d * xe + B * r * 4)
+    if cls == "stage2":
+        return len(n_list) * (F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8)
+    if cls == "truemask":
+        return len(n_list) * (F * d * w + F * 4 + B * d * xe + (B + 1) * F / 8)
+    if cls == "up":
+        return sum(n * (k_up * d * w + 4 + 4 + 4 * B) + F / 8 + B * d * xe for n in n_list)
+    if cls == "down":
+        return sum(n * (d * w + 4 + 4 * B) + B * d * 4 for n in n_list)
+    raise KeyError(cls)
+
+
+def step_bytes(layers, B, nlog_rows):
+    """Algorithmic bytes of every step: predictor (or true-mask GEMV), active rows and the
+    small vectors, from the measured union counts (nlog_rows[step][layer])."""
+    total = 0.0
+    for row in nlog_rows:
+        for L, n in zip(layers, row):
+            if L.rank > 0:
+                total += kernel_bytes("stage1", L, B, [n]) + kernel_bytes("stage2", L, B, [n])
+            else:
+                total += kernel_bytes("truemask", L, B, [n])
+            total += kernel_bytes("up", L, B, [n]) + kernel_bytes("down", L, B, [n])
+    return total
+
+
+def cpu_baseline(cfg, layers, x_tokens, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample: tokens chained through the stack."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    log(f"cpu baseline: copying {len(layers)} layers to host")
+    hosts = [L.to_host() for L in layers]
+    done_layers = 0
+    tokens = 0
+    elapsed = 0.0
+    t_all = x_tokens.cpu().numpy()
+    while elapsed < budget_s and tokens < t_all.shape[0]:
+        x = t_all[tokens:tokens + 1]
+        for H in hosts:
+            t0 = time.perf_counter()
+            r = oracle.layer_forward(H, x)
+            x = oracle.glue(r["y"], x)
+            elapsed += time.perf_counter() - t0
+            done_layers += 1
+            if elapsed >= budget_s and done_layers % len(hosts):
+                break
+        tokens += 1
+    token_equiv = done_layers / len(hosts)
+    return {"value": token_equiv / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_layers} layer passes ({token_equiv:.2f} tokens through the {len(hosts)}-layer stack, "
+                      f"batch 1, chained by the glue) in {elapsed:.1f} s of fp64 numpy compute; weight copies "
+                      f"to host not timed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).")
+        sys.exit(2)
+    import torch
+    import activation_sparse_ffn_layer_amd as pi
+    from synth import CONFIGS, make_tokens
+
+    cfg = CONFIGS[args.config]
+    if args.layers:
+        cfg = dataclasses.replace(cfg, layers=args.layers)
+    B = args.batch
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    max_rank = max(cfg.layer_rank(0.2), 8)
+    ctx = pi.Context(max_batch=B, max_d=cfg.d, max_ffn=cfg.ffn, max_rank=max_rank)
+    log(f"generating {cfg.layers} layers of {cfg.name} on the GPU")
+    t0 = time.perf_counter()
+    layers, ffns = build_stack(cfg, args.seed, pi, ctx)
+    log(f"  {sum(L.nbytes() for L in layers) / 1e9:.2f} GB of weights in {time.perf_counter() - t0:.1f} s")
+    T_w, T = args.warmup * B, args.steps * B
+    X = make_tokens(cfg, T_w + T, master=args.seed, device="cuda", stream=12345)
+    xw, xt = X[:T_w].contiguous(), X[T_w:].contiguous()
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    yw = torch.empty((max(T_w, B), cfg.d), dtype=torch.float32, device="cuda")
+    nlog = torch.zeros((args.steps, cfg.layers), dtype=torch.int32, device="cuda")
+    use_graph = not args.no_graph
+    if T_w:
+        pi.stack_run(ctx, ffns, xw, B, yw[:T_w], None, use_graph=use_graph)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    pi.stack_run(ctx, ffns, xt, B, y, nlog, use_graph=use_graph)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed_s = max(wall, gpu_ms / 1e3)
+    ms_per_step = elapsed_s * 1e3 / args.steps
+    value = T / elapsed_s
+    nl = nlog.cpu().numpy()
+    active_bytes = step_bytes(layers, B, nl.tolist())
+    frac_active = active_bytes / elapsed_s / (HBM_PEAK_GBS * 1e9)
+    log(f"timed: {args.steps} steps in {elapsed_s * 1e3:.2f} ms ({value:.1f} tok/s), "
+        f"{active_bytes / args.steps / 1e6:.1f} MB/step, {100 * frac_active:.1f}% of HBM peak on active bytes")
+
+    # per-kernel event pass on the first timed tokens
+    ps = min(args.profile_steps, args.steps)
+    nprof = torch.zeros((ps, cfg.layers), dtype=torch.int32, device="cuda")
+    yp = torch.empty((ps * B, cfg.d), dtype=torch.float32, device="cuda")
+    prof = pi.stack_profile(ctx, ffns, xt[:ps * B].contiguous(), B, yp, nprof)
+    npl = nprof.cpu().numpy()
+    kb = {}
+    for cls in ("stage1", "stage2", "truemask", "up", "down"):
+        tot = 0.0
+        for li, L in enumerate(layers):
+            if (cls in ("stage1", "stage2") and L.rank == 0) or (cls == "truemask" and L.rank > 0):
+                continue
+            tot += kernel_bytes(cls, L, B, npl[:, li].tolist())
+        kb[cls] = tot
+    # the reduction of the down partials moves no algorithmic bytes: it is reported, not ranked
+    dom = max((k for k in kb if prof[k][1] > 0), key=lambda k: prof[k][0])
+    for k, (ms, cnt) in prof.items():
+        if cnt:
+            gbs = kb.get(k, float("nan")) / (ms * 1e-3) / 1e9 if k in kb else float("nan")
+            log(f"  {k:9s} {cnt:6d} launches  avg {1e3 * ms / cnt:8.2f} us  {gbs:8.1f} GB/s")
+    dms, dcnt = prof[dom]
+    bytes_per_launch = kb[dom] / dcnt
+    achieved = bytes_per_launch / (dms / dcnt * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": round(bytes_per_launch), "avg_launch_us": round(1e3 * dms / dcnt, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, layers, xt[:B], args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f16": "f16", "f32": "f32", "q4_0": "q4_0+f16"}[cfg.wtype],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}-shaped {cfg.act} FFN stack", "layers": cfg.layers, "d": cfg.d,
+                   "ffn": cfg.ffn, "rank": cfg.rank, "weights": cfg.wtype, "batch": B, "seed": args.seed,
+                   "hot_first": cfg.hot_first, "graph": use_graph},
+        "hbm_frac_active": round(frac_active, 4),
+        "active_mb_per_step": round(active_bytes / args.steps / 1e6, 2),
+        "mean_active": round(float(nl.mean()) / cfg.ffn, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

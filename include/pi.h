@@ -1,0 +1,184 @@
+/*
+ * pi.h -- C ABI of the neuron-aware sparse FFN library (libpi.so) for AMD MI355X (gfx950).
+ *
+ * The library computes the FFN of a ReLU / ReGLU transformer layer by predicting which
+ * FFN neurons fire for the current token(s), compacting their indices, and reading and
+ * multiplying only those neurons' up/gate rows and down columns. This is the hot path of
+ * PowerInfer as described on the pages
+ *   P1 "Tüketici sınıfı GPU takılı PC'lerde yüksek hızlı büyük dil modeli serving",
+ *   P2 "PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU" (КПД),
+ *   P3 "PowerInfer: Mesin Inferensi LLM Cepat dengan GPU Konsumen" (unite.ai).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned, row-major.
+ *    The library never frees them. A pi_ffn borrows its weight pointers until destroyed.
+ *  - Compute entry points enqueue work on the context's HIP stream and return without
+ *    host synchronisation. Device faults surface at the caller's next synchronisation.
+ *  - Argument errors are detected on the host before anything is enqueued: the call
+ *    returns PI_ERR_INVALID (or PI_ERR_UNSUPPORTED) and enqueues nothing. HIP launch
+ *    failures return PI_ERR_HIP. pi_last_error(ctx) gives a human-readable reason.
+ *  - Compute entry points allocate nothing: every scratch buffer (activations, partial
+ *    sums, mask words, staging) belongs to the pi_ctx and is sized at pi_ctx_create.
+ *  - No C++ exception crosses this boundary. A pi_ctx is used by one host thread at a time.
+ *  - Neuron index space: the "stored" order of the layer's rows. With a hot-first layout
+ *    (pi_permute_rows), neuron_table[k] maps stored row k back to its original neuron.
+ */
+#ifndef PI_H
+#define PI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PI_ABI_VERSION 1
+
+typedef enum {
+  PI_OK = 0,
+  PI_ERR_INVALID = 1,      /* bad argument: null pointer, bad shape, misalignment, too large */
+  PI_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. batch size outside a path)     */
+  PI_ERR_OOM = 3,          /* device allocation failed in pi_ctx_create                      */
+  PI_ERR_HIP = 4           /* a HIP runtime call failed; see pi_last_error                    */
+} pi_status;
+
+/* Activation families the method supports (P1 header bullets, «Kısıtlar ve SSS»). */
+typedef enum { PI_ACT_RELU = 0, PI_ACT_REGLU = 1 } pi_act;
+
+/* Weight storage. PI_W_Q4_0: each block of 32 consecutive elements of a row stores an fp16
+ * scale s and 32 4-bit codes q; the weight is (q - 8) * s (P1 «Kuantizasyon ve uyumluluk»).
+ * Layout is struct-of-arrays: codes uint8 [rows][d/32][16], byte j of a block holding
+ * element j in its low nibble and element j+16 in its high nibble; scales fp16 [rows][d/32]. */
+typedef enum { PI_W_F32 = 0, PI_W_F16 = 1, PI_W_Q4_0 = 2 } pi_wtype;
+
+typedef struct pi_ctx pi_ctx;
+typedef struct pi_ffn pi_ffn;
+
+/* One FFN layer (borrowed device pointers). Neuron-major layout: row i of w_up / w_gate is
+ * neuron i's input row, row i of w_down_t is neuron i's output column (W_down transposed),
+ * so an active neuron's weights are contiguous rows (P3 «Operator yang Sadar Neuron»).
+ *   d        model width, multiple of 8 (of 32 for Q4_0)
+ *   ffn      number of FFN neurons, multiple of 64
+ *   rank     predictor rank r (multiple of 8, at most 2048; fp16 / Q4_0 layers only), or 0:
+ *            no predictor, the mask is the true pre-activation of the masked projection
+ *            (> threshold)
+ *   act      pi_act. ReLU masks the up projection; ReGLU masks the gate.
+ *   wtype    pi_wtype of w_up / w_gate / w_down_t
+ *   threshold decision threshold on the predictor logit (0 == "sigmoid > 0.5")
+ *   w_up, w_gate, w_down_t   [ffn][d] (fp32 / fp16) or Q4_0 codes; w_gate NULL for ReLU
+ *   s_up, s_gate, s_down     Q4_0 fp16 scales [ffn][d/32]; NULL otherwise
+ *   b        fp32 [ffn] bias of the masked projection (up for ReLU, gate for ReGLU)
+ *   p_w1     fp16 [rank][d], p_w2 fp16 [ffn][rank], p_b fp32 [ffn]: the low-rank predictor
+ *            logit = p_w2 (p_w1 x) + p_b (P3 «Prediktor Kepadatan Adaptif»); NULL if rank 0
+ *   neuron_table  int32 [ffn] stored row -> original neuron id, or NULL (identity).
+ *            Informational: outputs are in stored order. */
+typedef struct pi_ffn_desc {
+  int32_t d, ffn, rank;
+  int32_t act;
+  int32_t wtype;
+  float threshold;
+  const void *w_up, *w_gate, *w_down_t;
+  const uint16_t *s_up, *s_gate, *s_down;
+  const float *b;
+  const uint16_t *p_w1, *p_w2;
+  const float *p_b;
+  const int32_t *neuron_table;
+} pi_ffn_desc;
+
+int32_t pi_abi_version(void);
+const char *pi_status_str(pi_status s);
+/* Reason of the last failed call on ctx (empty string if none). Valid until the next call. */
+const char *pi_last_error(const pi_ctx *ctx);
+
+/* Create a context bound to `device` and the HIP stream `hip_stream` (hipStream_t, may be
+ * NULL for the default stream). Sizes the scratch for batches up to max_batch tokens and
+ * layers up to max_d x max_ffn with predictor rank up to max_rank. Allocates device memory. */
+pi_status pi_ctx_create(int32_t device, void *hip_stream, int32_t max_batch, int32_t max_d,
+                        int32_t max_ffn, int32_t max_rank, pi_ctx **out);
+void pi_ctx_destroy(pi_ctx *ctx);
+/* Rebind the context to another stream on the same device. */
+pi_status pi_ctx_set_stream(pi_ctx *ctx, void *hip_stream);
+
+/* Validate a layer description against the context and wrap it. Copies the descriptor,
+ * not the weights. */
+pi_status pi_ffn_create(pi_ctx *ctx, const pi_ffn_desc *desc, pi_ffn **out);
+void pi_ffn_destroy(pi_ffn *ffn);
+
+/* Predict the active neurons of B tokens (P3 «Fase Online», «Prediktor Kepadatan Adaptif»).
+ *   x         [B][d] fp16 (fp32 when wtype == PI_W_F32)
+ *   mask      [B][ffn/64] uint64 per-token bits: bit j of word w is neuron 64w+j, set when
+ *             the decision value (predictor logit, or true pre-activation if rank 0) is
+ *             strictly above the threshold
+ *   idx       [ffn] int32: ascending indices of the UNION of the B masks (the token's own
+ *             list when B == 1); entries at and beyond n_active are unspecified
+ *   n_active  device int32 scalar: length of idx
+ *   logits_out nullable fp32 [B][ffn]: the decision values themselves (for checking)
+ *   B         1..max_batch; 1..8 run on the vector units, 16..max_batch on matrix cores */
+pi_status pi_predict(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, uint64_t *mask,
+                     int32_t *idx, int32_t *n_active, float *logits_out);
+
+/* The neuron-aware sparse FFN on a given index list (P3 «Operator yang Sadar Neuron»): for
+ * every listed neuron i, a_t,i = relu(w_up[i].x_t + b_i) (ReLU) or
+ * relu(w_gate[i].x_t + b_i) * (w_up[i].x_t) (ReGLU), and y_t = sum_i a_t,i w_down_t[i].
+ * The one list applies to all B tokens.
+ *   idx, n_active  device [ffn] int32 (each entry < ffn, no duplicates) and device int32
+ *   y         [B][d] fp32 output (overwritten) */
+pi_status pi_sparse_ffn(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B,
+                        const int32_t *idx, const int32_t *n_active, float *y);
+
+/* pi_predict followed by pi_sparse_ffn on its union list. mask, idx and n_active are
+ * nullable outputs (context scratch is used when NULL). */
+pi_status pi_layer(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, float *y,
+                   uint64_t *mask, int32_t *idx, int32_t *n_active);
+
+/* Threshold + compaction alone, on caller-provided decision values v [B][ffn] fp32:
+ * the same device code pi_predict uses after computing v. */
+pi_status pi_compact(pi_ctx *ctx, const float *v, int32_t B, int32_t ffn, float threshold,
+                     uint64_t *mask, int32_t *idx, int32_t *n_active);
+
+/* Chain between stacked layers: x_out_t = round(y_t / sqrt(mean(y_t^2))) to x's storage
+ * type (fp16, or fp32 when x_is_f32), or x_prev_t unchanged when y_t is all zero.
+ *   y [B][d] fp32, x_prev [B][d], x_out [B][d] */
+pi_status pi_glue(pi_ctx *ctx, const float *y, const void *x_prev, int32_t B, int32_t d,
+                  int32_t x_is_f32, void *x_out);
+
+/* Run L layers over T tokens, B tokens per step (T % B == 0), one step at a time: step s
+ * feeds x_tokens[s*B..s*B+B) to layer 0, each layer's y (through pi_glue) to the next, and
+ * writes the last layer's y to y_out[s*B..]. Token-by-token decode (P3 intro) at B == 1.
+ *   layers     host array of L layer handles with equal d and activation/weight types
+ *   x_tokens   [T][d] fp16 (fp32 for PI_W_F32 stacks); y_out [T][d] fp32
+ *   n_active_log nullable device int32 [T/B][L]: n_active of every (step, layer)
+ *   use_graph  nonzero: each step's L layers run as one captured HIP graph */
+pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, const void *x_tokens,
+                       int32_t T, int32_t B, float *y_out, int32_t *n_active_log, int32_t use_graph);
+
+/* Kernel classes of pi_stack_profile's outputs, in this order:
+ * predictor stage 1, predictor stage 2 + threshold, true-mask threshold GEMV, gathered
+ * up/gate GEMV (with the index scan), down-projection partials, partial reduction. */
+#define PI_KERNEL_CLASSES 6
+
+/* pi_stack_run without a graph, with a hipEvent pair recorded on the context's stream around
+ * every kernel launch. Blocks until the work is done, then writes the summed event time in
+ * milliseconds (ms_out[PI_KERNEL_CLASSES], host) and the number of launches
+ * (launches_out[PI_KERNEL_CLASSES], host) of each kernel class. Other arguments as for
+ * pi_stack_run. For measurement; the events add a little dispatch time to every launch. */
+pi_status pi_stack_profile(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, const void *x_tokens,
+                           int32_t T, int32_t B, float *y_out, int32_t *n_active_log, double *ms_out,
+                           int64_t *launches_out);
+
+/* Hot-first neuron order (P3 «Penempatan dan Pengelolaan Neuron»): perm[k] = the neuron
+ * with the k-th largest activation probability, ties in ascending neuron order. HOST
+ * pointers: p double [ffn], perm int32 [ffn]. */
+pi_status pi_hot_first_order(const double *p, int32_t ffn, int32_t *perm);
+
+/* Gather rows on the device: dst[k] = src[perm[k]] for k < rows, each row_bytes long
+ * (a multiple of 4). Used to store a layer's neuron-indexed arrays in hot-first order.
+ * perm is a device int32 [rows] permutation; src and dst must not overlap. */
+pi_status pi_permute_rows(pi_ctx *ctx, const void *src, void *dst, const int32_t *perm,
+                          int32_t rows, int64_t row_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PI_H */

@@ -1,0 +1,294 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on seeded synthetic inputs.
+
+Masks: bit exact outside the exclusion band |v| < 1e-4 (band neurons counted). Index
+lists: bit exact with the mask they come from. Decision values: within the band width of
+the oracle's. y: max per-token relative L2 within 1e-5 (fp32 weights), 2e-3 (fp16),
+1e-2 (Q4_0). Identical decision values (pi_compact): bit exact with no exclusion.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, make_decision_values, make_layer, make_tokens
+from tests.parity_util import TOL, check_layer, make_ctx, rel_l2, run_layer, words_to_bool
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import activation_sparse_ffn_layer_amd as pi
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ threshold + compaction
+
+@pytest.mark.parametrize("B,ffn", [(1, 64), (1, 2048), (2, 320), (5, 16384), (8, 49152), (1, 49152)])
+def test_compact_identical_decision_values(B, ffn):
+    _say(f"compact B={B} ffn={ffn}")
+    v = make_decision_values(B, ffn, seed=1000 * B + ffn)
+    ctx = pi.Context(max_batch=8, max_d=64, max_ffn=ffn, max_rank=0)
+    vd = torch.from_numpy(v).cuda()
+    mask = torch.zeros((B, ffn // 64), dtype=torch.int64, device="cuda")
+    idx = torch.full((ffn,), -1, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    pi.compact(ctx, vd, 0.0, mask, idx, n)
+    torch.cuda.synchronize()
+    m = oracle.threshold(v, 0.0)
+    np.testing.assert_array_equal(mask.cpu().numpy().view(np.uint64), oracle.mask_words(m))
+    ref = oracle.compact(oracle.union(m))
+    assert int(n.item()) == ref.size
+    np.testing.assert_array_equal(idx[:ref.size].cpu().numpy(), ref)
+
+
+def test_compact_every_low_pattern():
+    """All 4096 patterns of a word's low 12 bits (plus random high bits), 64 words per call."""
+    ffn = 64 * 64
+    ctx = pi.Context(max_batch=1, max_d=64, max_ffn=ffn, max_rank=0)
+    rng = np.random.default_rng(7)
+    mask = torch.zeros((1, ffn // 64), dtype=torch.int64, device="cuda")
+    idx = torch.full((ffn,), -1, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    for call in range(64):
+        pats = np.arange(call * 64, call * 64 + 64)
+        bits = np.zeros((64, 64), dtype=bool)
+        for j in range(12):
+            bits[:, j] = (pats >> j) & 1
+        bits[:, 12:] = rng.random((64, 52)) < 0.3
+        v = np.where(bits.reshape(1, ffn), 1.0, -1.0).astype(np.float32)
+        pi.compact(ctx, torch.from_numpy(v).cuda(), 0.0, mask, idx, n)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(words_to_bool(mask, ffn)[0], bits.reshape(ffn))
+        ref = oracle.compact(bits.reshape(ffn))
+        assert int(n.item()) == ref.size
+        np.testing.assert_array_equal(idx[:ref.size].cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------------ layer parity
+
+def _cfg(name, **kw):
+    return dataclasses.replace(CONFIGS[name], **kw)
+
+
+CASES = {
+    # name: (config, layer id, tokens, batch)
+    "tiny": (_cfg("tiny"), 0, 16, 1),
+    "opt-small": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 0, 8, 1),
+    "opt-full": (_cfg("opt6.7b"), 3, 3, 1),
+    "falcon-full-r1024": (_cfg("falcon40b"), 0, 2, 1),
+    "llama-full-reglu": (_cfg("llama70b"), 0, 2, 1),
+    "llama-small-truemask": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 0, 4, 1),
+    "opt175-full-q4": (_cfg("opt175b"), 0, 2, 1),
+    "opt175-small-q4-b2": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 0, 4, 2),
+    "q4-truemask-ragged": (_cfg("opt175b", d=544, ffn=320, rank=None), 0, 4, 1),
+    "f16-ragged": (_cfg("opt6.7b", d=520, ffn=320, rank=136), 0, 4, 1),
+    "f16-b2": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 1, 8, 2),
+    "f16-b4": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 1, 8, 4),
+    "f16-b8": (_cfg("opt6.7b", d=2048, ffn=8192, rank=1024), 1, 16, 8),
+    "reglu-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 1, 8, 8),
+    "f32-b3": (_cfg("tiny"), 0, 9, 3),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_layer_parity(case):
+    cfg, li, T, B = CASES[case]
+    _say(f"layer parity {case}: d={cfg.d} ffn={cfg.ffn} rank={cfg.rank} {cfg.wtype} {cfg.act} B={B}")
+    L = make_layer(cfg, li, device="cuda")
+    H = L.to_host()
+    X = make_tokens(cfg, T, device="cuda", stream=li + 1)
+    ctx = make_ctx([L], max_batch=8)
+    ffn = pi.Ffn(ctx, L)
+    bands = flips = 0
+    for s in range(T // B):
+        x = X[s * B:(s + 1) * B].contiguous()
+        out = run_layer(ctx, ffn, x, with_logits=True)
+        nb, nf = check_layer(H, x.cpu().numpy(), out, TOL[cfg.wtype], check_logits=True)
+        bands += nb
+        flips += nf
+    _say(f"  {case}: band neurons {bands}, decided differently {flips}")
+
+
+def test_empty_and_full_masks():
+    cfg = _cfg("opt6.7b", d=1024, ffn=2048, rank=512)
+    L = make_layer(cfg, 0, device="cuda")
+    x = make_tokens(cfg, 2, device="cuda")
+    ctx = make_ctx([L])
+    for bias, expect in ((-60.0, 0), (60.0, cfg.ffn)):
+        L2 = dataclasses.replace(L, b=torch.full_like(L.b, bias), p_b=torch.full_like(L.p_b, bias))
+        ffn = pi.Ffn(ctx, L2)
+        out = run_layer(ctx, ffn, x[:1])
+        assert int(out["n"].item()) == expect
+        check_layer(L2.to_host(), x[:1].cpu().numpy(), out, TOL["f16"])
+        if expect == 0:
+            assert torch.all(out["y"] == 0)
+
+
+def test_predict_then_sparse_ffn_equals_layer_bitwise():
+    cfg = _cfg("opt6.7b", d=2048, ffn=8192, rank=512)
+    L = make_layer(cfg, 2, device="cuda")
+    x = make_tokens(cfg, 4, device="cuda")
+    ctx = make_ctx([L])
+    ffn = pi.Ffn(ctx, L)
+    for B in (1, 4):
+        xb = x[:B].contiguous()
+        out = run_layer(ctx, ffn, xb)
+        mask = torch.zeros_like(out["mask"])
+        idx = torch.full_like(out["idx"], -1)
+        n = torch.full_like(out["n"], -1)
+        pi.predict(ctx, ffn, xb, mask, idx, n)
+        y = torch.empty_like(out["y"])
+        pi.sparse_ffn(ctx, ffn, xb, idx, n, y)
+        torch.cuda.synchronize()
+        assert torch.equal(mask, out["mask"]) and int(n.item()) == int(out["n"].item())
+        assert torch.equal(y, out["y"])
+        out2 = run_layer(ctx, ffn, xb)
+        assert torch.equal(out2["y"], out["y"]), "layer is not deterministic"
+
+
+def test_sparse_ffn_on_oracle_index_list():
+    """pi_sparse_ffn on an index list the oracle computed (input-side: from synth data)."""
+    cfg = _cfg("llama70b", d=1024, ffn=4096, rank=None)
+    L = make_layer(cfg, 5, device="cuda")
+    H = L.to_host()
+    x = make_tokens(cfg, 2, device="cuda")
+    ctx = make_ctx([L])
+    ffn = pi.Ffn(ctx, L)
+    xh = x.cpu().numpy()
+    idx_h = oracle.compact(oracle.union(oracle.threshold(oracle.decision_values(H, xh))))
+    idx = torch.from_numpy(np.concatenate([idx_h, np.zeros(cfg.ffn - idx_h.size, np.int32)])).cuda()
+    n = torch.tensor([idx_h.size], dtype=torch.int32, device="cuda")
+    y = torch.empty((2, cfg.d), dtype=torch.float32, device="cuda")
+    pi.sparse_ffn(ctx, ffn, x, idx, n, y)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_ffn(H, xh, idx_h)
+    for t in range(2):
+        assert rel_l2(y[t].cpu().numpy(), ref[t]) <= TOL["f16"]
+
+
+# ------------------------------------------------------------------------------- glue
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_glue(dtype):
+    rng = np.random.default_rng(11)
+    B, d = 3, 4096
+    y = rng.normal(0, 2.5, (B, d)).astype(np.float32)
+    y[1] = 0
+    xp = rng.normal(0, 1, (B, d)).astype(np.float16 if dtype == torch.float16 else np.float32)
+    ctx = pi.Context(max_batch=4, max_d=d, max_ffn=64, max_rank=0)
+    xo = torch.empty((B, d), dtype=dtype, device="cuda")
+    pi.glue(ctx, torch.from_numpy(y).cuda(), torch.from_numpy(xp).cuda(), xo)
+    torch.cuda.synchronize()
+    ref = oracle.glue(y.astype(np.float64), xp)
+    got = xo.cpu().numpy()
+    np.testing.assert_array_equal(got[1], xp[1])
+    if dtype == torch.float16:
+        # fp32 arithmetic then one rounding to fp16: at most one fp16 ulp from the fp64 result
+        ulp = np.spacing(np.abs(ref.astype(np.float16))).astype(np.float64)
+        assert np.all(np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= ulp)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------------------------ stacks
+
+def test_stack_true_mask_chain_matches_oracle():
+    cfg = _cfg("opt6.7b", layers=3, d=1024, ffn=4096, rank=None)
+    layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
+    X = make_tokens(cfg, 4, device="cuda")
+    ctx = make_ctx(layers, max_batch=1)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+    y = torch.empty((4, cfg.d), dtype=torch.float32, device="cuda")
+    nlog = torch.zeros((4, cfg.layers), dtype=torch.int32, device="cuda")
+    pi.stack_run(ctx, ffns, X, 1, y, nlog, use_graph=True)
+    y2 = torch.empty_like(y)
+    pi.stack_run(ctx, ffns, X, 1, y2, None, use_graph=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "graph and eager runs differ"
+    hosts = [L.to_host() for L in layers]
+    for t in range(4):
+        res = oracle.stack_forward(hosts, X[t:t + 1].cpu().numpy())
+        assert rel_l2(y[t].cpu().numpy(), res[-1]["y"][0]) <= TOL["f16"]
+        got_n = nlog[t].cpu().numpy()
+        want_n = np.array([r["n_active"] for r in res])
+        assert np.all(np.abs(got_n - want_n) <= 2), (got_n, want_n)
+
+
+def test_stack_predictor_graph_equals_eager_and_is_deterministic():
+    cfg = _cfg("opt6.7b", layers=4, d=1024, ffn=4096, rank=512)
+    layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
+    X = make_tokens(cfg, 8, device="cuda")
+    ctx = make_ctx(layers, max_batch=2)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+    outs = []
+    for use_graph in (True, True, False):
+        y = torch.empty((8, cfg.d), dtype=torch.float32, device="cuda")
+        pi.stack_run(ctx, ffns, X, 2, y, None, use_graph=use_graph)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    # the first layer of each step is teacher-free: check it against the oracle directly
+    H0 = layers[0].to_host()
+    out = run_layer(ctx, ffns[0], X[:2].contiguous())
+    check_layer(H0, X[:2].cpu().numpy(), out, TOL["f16"])
+
+
+# ------------------------------------------------------------------------ permutation
+
+def test_hot_first_permutation_on_device():
+    cfg = _cfg("falcon40b", d=1024, ffn=4096, rank=512)
+    L = make_layer(cfg, 7, device="cuda")
+    perm = pi.hot_first_order(L.p)
+    np.testing.assert_array_equal(perm, oracle.hot_first_order(L.p))
+    ctx = make_ctx([L])
+    pd = torch.from_numpy(perm).cuda()
+
+    def pr(t):
+        if t is None:
+            return None
+        out = torch.empty_like(t)
+        pi.permute_rows(ctx, t, out, pd)
+        return out
+
+    P = dataclasses.replace(L, w_up=pr(L.w_up), w_down_t=pr(L.w_down_t), b=pr(L.b), p_w2=pr(L.p_w2), p_b=pr(L.p_b))
+    torch.cuda.synchronize()
+    H, HP = L.to_host(), P.to_host()
+    ref = oracle.permute_layer(H, perm)
+    for k in ("w_up", "w_down_t", "b", "p_w2", "p_b"):
+        np.testing.assert_array_equal(HP[k], ref[k])
+    x = make_tokens(cfg, 2, device="cuda")
+    ffn_p = pi.Ffn(ctx, P, neuron_table=pd)
+    out = run_layer(ctx, ffn_p, x[:1])
+    check_layer(HP, x[:1].cpu().numpy(), out, TOL["f16"])
+    ffn = pi.Ffn(ctx, L)
+    out0 = run_layer(ctx, ffn, x[:1])
+    assert rel_l2(out["y"].cpu().numpy(), out0["y"].cpu().numpy()) <= TOL["f16"]
+
+
+# ----------------------------------------------------------------------------- errors
+
+def test_invalid_arguments_enqueue_nothing():
+    cfg = _cfg("opt6.7b", d=1024, ffn=2048, rank=512)
+    L = make_layer(cfg, 0, device="cuda")
+    ctx = make_ctx([L], max_batch=2)
+    ffn = pi.Ffn(ctx, L)
+    x = make_tokens(cfg, 4, device="cuda")
+    y = torch.empty((4, cfg.d), dtype=torch.float32, device="cuda")
+    with pytest.raises(pi.PiError, match="invalid argument"):
+        pi.layer(ctx, ffn, x, y)                       # B = 4 > max_batch 2
+    with pytest.raises(pi.PiError, match="not 16-byte aligned"):
+        pi.layer(ctx, ffn, x[:1], y.view(-1)[1:].view(-1)[: cfg.d].view(1, cfg.d))
+    bad = dataclasses.replace(L, ffn=2000)
+    with pytest.raises(pi.PiError, match="multiple of 64"):
+        pi.Ffn(ctx, bad)
+    big = pi.Context(max_batch=16, max_d=1024, max_ffn=2048, max_rank=512)
+    f2 = pi.Ffn(big, L)
+    x16 = make_tokens(cfg, 16, device="cuda")
+    y16 = torch.empty((16, cfg.d), dtype=torch.float32, device="cuda")
+    with pytest.raises(pi.PiError, match="unsupported"):
+        pi.layer(big, f2, x16[:12].contiguous(), y16[:12])
