@@ -62,6 +62,27 @@ __device__ __forceinline__ float transpose_reduce(float (&acc)[R], int lane) {
   return v;
 }
 
+// transpose_reduce over the lanes that agree in their low S bits: lane groups of 2^S lanes
+// carry different columns. On return every lane holds the full sum (over the 64 >> S lanes
+// of its group) of value ((lane >> S) & (R-1)).
+template <int R, int S>
+__device__ __forceinline__ float transpose_reduce_s(float (&acc)[R], int lane) {
+#pragma unroll
+  for (int o = R / 2; o >= 1; o >>= 1) {
+    const bool hi = (lane & (o << S)) != 0;
+#pragma unroll
+    for (int i = 0; i < o; ++i) {
+      float send = hi ? acc[i] : acc[i + o];
+      float keep = hi ? acc[i + o] : acc[i];
+      acc[i] = keep + __shfl_xor(send, o << S, WAVE);
+    }
+  }
+  float v = acc[0];
+#pragma unroll
+  for (int o = R << S; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
 // Block-wide sum of one float per thread (BLOCK threads). Uses `red` [NWAVES] in LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);

@@ -28,8 +28,8 @@ struct pi_ctx {
   uint64_t* munion = nullptr;   // [max_ffn/64]
   int32_t* idx = nullptr;       // [max_ffn]
   int32_t* nbuf = nullptr;      // [16]
-  float* a = nullptr;           // [max_batch][max_ffn]
-  float* part = nullptr;        // [G_MAX][max_batch][max_d]
+  float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
+  float* part = nullptr;        // [DOWN_G][max_batch][max_d] down-projection partial sums
   float* y = nullptr;           // [max_batch][max_d]
   uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
   uint8_t* xstage = nullptr;    // [max_batch][max_d] fp32-sized
@@ -55,7 +55,6 @@ struct pi_ffn {
 
 namespace {
 
-constexpr int G_MAX = 64;
 constexpr int NLOG_CAP = 4096;
 
 pi_status fail(pi_ctx* ctx, pi_status s, const char* fmt, ...) {
@@ -160,156 +159,178 @@ pi_status launch_stage1(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
   }
 }
 
-template <int NB, int CPL>
-pi_status launch_stage2_t(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits) {
-  constexpr int RPW = NB == 1 ? 16 : NB == 2 ? 8 : NB == 4 ? 4 : 2;
+// Stage 2 of the predictor; with `up`, also the activations of each workgroup's own active
+// neurons (x read from `x`, a dense [B][ffn]).
+constexpr int STAGE2_TILE = 32;  // neurons per workgroup in predictor stage 2
+
+template <int NB, int CPL, bool UP, int WT, int ACT>
+pi_status launch_stage2_t(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
+  const size_t lds = UP ? (size_t)NB * L.d * (WT == W_F32 ? 4 : 2) : 0;
+  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
+  auto kern = k_stage2<NB, CPL, STAGE2_TILE, UP, WT, ACT>;
+  PI_HIP(c, allow_lds(kern, lds));
   ProfScope ps(c, K_STAGE2);
-  hipLaunchKernelGGL((k_stage2<NB, CPL, RPW>), dim3(L.ffn / 64), dim3(BLOCK), 0, c->stream, L, c->z, B, mtok,
-                     c->munion, logits);
+  hipLaunchKernelGGL(kern, dim3(L.ffn / STAGE2_TILE), dim3(BLOCK), lds, c->stream, L, c->z, B, mtok, c->munion,
+                     logits, x, c->a);
   PI_HIP(c, hipGetLastError());
   return PI_OK;
 }
 
-template <int NB>
-pi_status launch_stage2_nb(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits) {
-  const int cpl = (L.rank + 511) / 512;
-  if (cpl <= 1) return launch_stage2_t<NB, 1>(c, L, B, mtok, logits);
-  if (cpl <= 2) return launch_stage2_t<NB, 2>(c, L, B, mtok, logits);
-  return launch_stage2_t<NB, 4>(c, L, B, mtok, logits);
+template <int NB, int CPL>
+pi_status launch_stage2_c(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
+  if (x == nullptr) return launch_stage2_t<NB, CPL, false, W_F16, ACT_RELU>(c, L, B, mtok, logits, x);
+  if (L.wtype == W_F16)
+    return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_F16, ACT_RELU>(c, L, B, mtok, logits, x)
+                             : launch_stage2_t<NB, CPL, true, W_F16, ACT_REGLU>(c, L, B, mtok, logits, x);
+  if constexpr (NB <= 2) {
+    if (L.wtype == W_Q4)
+      return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_Q4, ACT_RELU>(c, L, B, mtok, logits, x)
+                               : launch_stage2_t<NB, CPL, true, W_Q4, ACT_REGLU>(c, L, B, mtok, logits, x);
+  }
+  return fail(c, PI_ERR_UNSUPPORTED, "no predictor path for this weight type and batch");
 }
 
-pi_status launch_stage2(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits) {
+template <int NB>
+pi_status launch_stage2_nb(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
+  if (L.rank <= 512) return launch_stage2_c<NB, 1>(c, L, B, mtok, logits, x);
+  return launch_stage2_c<NB, 2>(c, L, B, mtok, logits, x);
+}
+
+pi_status launch_stage2(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
   switch (nb_for(B)) {
-    case 1: return launch_stage2_nb<1>(c, L, B, mtok, logits);
-    case 2: return launch_stage2_nb<2>(c, L, B, mtok, logits);
-    case 4: return launch_stage2_nb<4>(c, L, B, mtok, logits);
-    default: return launch_stage2_nb<8>(c, L, B, mtok, logits);
+    case 1: return launch_stage2_nb<1>(c, L, B, mtok, logits, x);
+    case 2: return launch_stage2_nb<2>(c, L, B, mtok, logits, x);
+    case 4: return launch_stage2_nb<4>(c, L, B, mtok, logits, x);
+    default: return launch_stage2_nb<8>(c, L, B, mtok, logits, x);
   }
 }
 
-template <int WT, int NB>
+template <int WT, int NB, bool UP>
 pi_status launch_truemask_t(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
   constexpr bool XF32 = WT == W_F32;
   const size_t lds = (size_t)NB * L.d * (XF32 ? 4 : 2);
   if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
-  PI_HIP(c, allow_lds(k_truemask<WT, NB, XF32>, lds));
+  auto kern = k_truemask<WT, NB, XF32, UP>;
+  PI_HIP(c, allow_lds(kern, lds));
   ProfScope ps(c, K_TRUEMASK);
-  hipLaunchKernelGGL((k_truemask<WT, NB, XF32>), dim3(L.ffn / 64), dim3(BLOCK), lds, c->stream, L, xin, B, mtok,
-                     c->munion, logits);
+  hipLaunchKernelGGL(kern, dim3(L.ffn / 64), dim3(BLOCK), lds, c->stream, L, xin, B, mtok, c->munion, logits, c->a);
   PI_HIP(c, hipGetLastError());
   return PI_OK;
 }
 
-template <int WT>
+template <int WT, bool UP>
 pi_status launch_truemask_w(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
   switch (nb_for(B)) {
-    case 1: return launch_truemask_t<WT, 1>(c, L, xin, B, mtok, logits);
-    case 2: return launch_truemask_t<WT, 2>(c, L, xin, B, mtok, logits);
-    case 4: return launch_truemask_t<WT, 4>(c, L, xin, B, mtok, logits);
-    default: return launch_truemask_t<WT, 8>(c, L, xin, B, mtok, logits);
+    case 1: return launch_truemask_t<WT, 1, UP>(c, L, xin, B, mtok, logits);
+    case 2: return launch_truemask_t<WT, 2, UP>(c, L, xin, B, mtok, logits);
+    case 4: if constexpr (WT != W_Q4) return launch_truemask_t<WT, 4, UP>(c, L, xin, B, mtok, logits); break;
+    default: if constexpr (WT != W_Q4) return launch_truemask_t<WT, 8, UP>(c, L, xin, B, mtok, logits); break;
   }
+  return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
 }
 
-pi_status launch_truemask(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
+pi_status launch_truemask(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits,
+                          bool up) {
   switch (L.wtype) {
-    case W_F32: return launch_truemask_w<W_F32>(c, L, xin, B, mtok, logits);
-    case W_F16: return launch_truemask_w<W_F16>(c, L, xin, B, mtok, logits);
-    default: return launch_truemask_w<W_Q4>(c, L, xin, B, mtok, logits);
+    case W_F32: return up ? launch_truemask_w<W_F32, true>(c, L, xin, B, mtok, logits)
+                          : launch_truemask_w<W_F32, false>(c, L, xin, B, mtok, logits);
+    case W_F16: return up ? launch_truemask_w<W_F16, true>(c, L, xin, B, mtok, logits)
+                          : launch_truemask_w<W_F16, false>(c, L, xin, B, mtok, logits);
+    default: return up ? launch_truemask_w<W_Q4, true>(c, L, xin, B, mtok, logits)
+                       : launch_truemask_w<W_Q4, false>(c, L, xin, B, mtok, logits);
   }
 }
 
-int up_grid(const pi_ctx* c, const LayerDev& L) {
-  return std::max(1, std::min((L.ffn + NWAVES - 1) / NWAVES, 2 * c->cus));
-}
-
-template <int WT, int ACT, int NB, bool SCAN>
-pi_status launch_up_t(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in,
-                      const int32_t* n_in, int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
-  const size_t xe = (WT == W_F32) ? 4 : 2;
-  const int W = L.ffn / 64;
-  const size_t lds = (size_t)NB * L.d * xe + (SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
+template <int WT, int ACT, int NB>
+pi_status launch_up_t(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
+  const size_t lds = (size_t)NB * L.d * (WT == W_F32 ? 4 : 2);
   if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
-  PI_HIP(c, allow_lds(k_up<WT, ACT, NB, SCAN>, lds));
+  auto kern = k_up<WT, ACT, NB>;
+  PI_HIP(c, allow_lds(kern, lds));
+  const int per = (ACT == ACT_RELU) ? 2 : 1;
+  const int grid = std::max(1, std::min((L.ffn + NWAVES * per - 1) / (NWAVES * per), 2 * c->cus));
   ProfScope ps(c, K_UP);
-  hipLaunchKernelGGL((k_up<WT, ACT, NB, SCAN>), dim3(up_grid(c, L)), dim3(BLOCK), lds, c->stream, L, x, B, c->munion,
-                     idx_in, n_in, idx_out, n_out, n_log, c->a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, c->stream, L, x, B, idx_in, n_in, c->a);
   PI_HIP(c, hipGetLastError());
   return PI_OK;
 }
 
-template <int WT, int ACT, bool SCAN>
-pi_status launch_up_a(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in,
-                      int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+template <int WT, int ACT>
+pi_status launch_up_a(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
   switch (nb_for(B)) {
-    case 1: return launch_up_t<WT, ACT, 1, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-    case 2: return launch_up_t<WT, ACT, 2, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-    case 4: return launch_up_t<WT, ACT, 4, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-    default: return launch_up_t<WT, ACT, 8, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    case 1: return launch_up_t<WT, ACT, 1>(c, L, x, B, idx_in, n_in);
+    case 2: return launch_up_t<WT, ACT, 2>(c, L, x, B, idx_in, n_in);
+    case 4: if constexpr (WT != W_Q4) return launch_up_t<WT, ACT, 4>(c, L, x, B, idx_in, n_in); break;
+    default: if constexpr (WT != W_Q4) return launch_up_t<WT, ACT, 8>(c, L, x, B, idx_in, n_in); break;
   }
+  return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
 }
 
-template <bool SCAN>
-pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in,
-                    int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
   if (L.act == ACT_RELU) {
     switch (L.wtype) {
-      case W_F32: return launch_up_a<W_F32, ACT_RELU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-      case W_F16: return launch_up_a<W_F16, ACT_RELU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-      default: return launch_up_a<W_Q4, ACT_RELU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+      case W_F32: return launch_up_a<W_F32, ACT_RELU>(c, L, x, B, idx_in, n_in);
+      case W_F16: return launch_up_a<W_F16, ACT_RELU>(c, L, x, B, idx_in, n_in);
+      default: return launch_up_a<W_Q4, ACT_RELU>(c, L, x, B, idx_in, n_in);
     }
   }
   switch (L.wtype) {
-    case W_F32: return launch_up_a<W_F32, ACT_REGLU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-    case W_F16: return launch_up_a<W_F16, ACT_REGLU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
-    default: return launch_up_a<W_Q4, ACT_REGLU, SCAN>(c, L, x, B, idx_in, n_in, idx_out, n_out, n_log);
+    case W_F32: return launch_up_a<W_F32, ACT_REGLU>(c, L, x, B, idx_in, n_in);
+    case W_F16: return launch_up_a<W_F16, ACT_REGLU>(c, L, x, B, idx_in, n_in);
+    default: return launch_up_a<W_Q4, ACT_REGLU>(c, L, x, B, idx_in, n_in);
   }
 }
 
-int slice_width(int wtype) {
-  return wtype == W_F16 ? DownGeom<W_F16>::SW : wtype == W_F32 ? DownGeom<W_F32>::SW : DownGeom<W_Q4>::SW;
-}
+// Down projection over the active neurons into DOWN_G partial sums (from the union words,
+// SCAN, which also writes idx and n; or from a given index list), then their reduction into y.
+constexpr int DOWN_G = 16;
 
-int down_groups(const LayerDev& L) {
-  const int S = (L.d + slice_width(L.wtype) - 1) / slice_width(L.wtype);
-  return std::max(8, std::min(G_MAX, 1024 / S));
-}
-
-template <int WT, int NB>
-pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx, const int32_t* n, int G) {
+template <int WT, int NB, bool SCAN>
+pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
+                        int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+  constexpr int SEG = DownGeom<WT>::SEG;
+  constexpr int U = (WT == W_Q4) ? (NB == 1 ? 4 : 2) : (NB >= 4 ? 4 : 8);
+  const int W = L.ffn / 64;
+  const size_t lds = SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 + (size_t)IDX_LDS * 4 : 0;
+  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the index scan", L.ffn);
+  auto kern = k_down_part<WT, NB, SCAN, SEG, U, DOWN_G>;
+  PI_HIP(c, allow_lds(kern, lds));
   const int S = (L.d + DownGeom<WT>::SW - 1) / DownGeom<WT>::SW;
-  ProfScope ps(c, K_DOWN);
-  hipLaunchKernelGGL((k_down<WT, NB>), dim3(G, S), dim3(BLOCK), 0, c->stream, L, B, idx, n, c->a, c->part, G);
+  {
+    ProfScope ps(c, K_DOWN);
+    hipLaunchKernelGGL(kern, dim3(DOWN_G, S), dim3(BLOCK), lds, c->stream, L, B, c->munion, idx_in, n_in, c->a,
+                       c->part, DOWN_G, idx_out, n_out, n_log);
+  }
+  PI_HIP(c, hipGetLastError());
+  const int BD = B * L.d;
+  {
+    ProfScope ps(c, K_REDUCE);
+    hipLaunchKernelGGL(k_reduce, dim3((BD + WAVE - 1) / WAVE), dim3(BLOCK), 0, c->stream, c->part, DOWN_G, BD, y);
+  }
   PI_HIP(c, hipGetLastError());
   return PI_OK;
 }
 
-template <int WT>
-pi_status launch_down_w(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx, const int32_t* n, int G) {
+template <int WT, bool SCAN>
+pi_status launch_down_w(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
+                        int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
   switch (nb_for(B)) {
-    case 1: return launch_down_t<WT, 1>(c, L, B, idx, n, G);
-    case 2: return launch_down_t<WT, 2>(c, L, B, idx, n, G);
-    case 4: if constexpr (WT != W_Q4) return launch_down_t<WT, 4>(c, L, B, idx, n, G); break;
-    default: if constexpr (WT != W_Q4) return launch_down_t<WT, 8>(c, L, B, idx, n, G); break;
+    case 1: return launch_down_t<WT, 1, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    case 2: return launch_down_t<WT, 2, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    case 4: if constexpr (WT != W_Q4) return launch_down_t<WT, 4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log); break;
+    default: if constexpr (WT != W_Q4) return launch_down_t<WT, 8, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log); break;
   }
   return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 down projection supports batch <= 2 on this path");
 }
 
-pi_status launch_down_reduce(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx, const int32_t* n, float* y) {
-  const int G = down_groups(L);
-  pi_status s;
+template <bool SCAN>
+pi_status launch_down(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
+                      int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
   switch (L.wtype) {
-    case W_F32: s = launch_down_w<W_F32>(c, L, B, idx, n, G); break;
-    case W_F16: s = launch_down_w<W_F16>(c, L, B, idx, n, G); break;
-    default: s = launch_down_w<W_Q4>(c, L, B, idx, n, G); break;
+    case W_F32: return launch_down_w<W_F32, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    case W_F16: return launch_down_w<W_F16, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    default: return launch_down_w<W_Q4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
   }
-  if (s != PI_OK) return s;
-  const int BD = B * L.d;
-  {
-    ProfScope ps(c, K_REDUCE);
-    hipLaunchKernelGGL(k_reduce, dim3((BD + WAVE - 1) / WAVE), dim3(BLOCK), 0, c->stream, c->part, G, BD, y);
-  }
-  PI_HIP(c, hipGetLastError());
-  return PI_OK;
 }
 
 pi_status launch_compact(pi_ctx* c, int ffn, int32_t* idx, int32_t* n) {
@@ -343,20 +364,19 @@ pi_status check_dev_ptr(pi_ctx* c, const void* p, const char* name, bool nullabl
     if (s_ != PI_OK) return s_;      \
   } while (0)
 
-// Enqueue the whole layer for one batch. xin: where x comes from; x_cur: the layer's input
-// in global memory as the up kernel reads it (equal to xin.x, or xin.x_out in glue mode).
+// Enqueue the whole layer for one batch: three kernels. xin: where x comes from; x_cur: the
+// layer's input in global memory as the activation step reads it (xin.x, or xin.x_out when
+// xin applies the glue; written by workgroup 0 of the first kernel).
 pi_status enqueue_layer(pi_ctx* c, const pi_ffn* f, const XIn& xin, const void* x_cur, int B, float* y,
                         uint64_t* mask, int32_t* idx, int32_t* n, int32_t* n_log) {
   const LayerDev L = to_dev(f->desc);
   if (L.rank > 0) {
     PI_TRY(launch_stage1(c, L, xin, B));
-    PI_TRY(launch_stage2(c, L, B, mask, nullptr));
+    PI_TRY(launch_stage2(c, L, B, mask, nullptr, x_cur));
   } else {
-    PI_TRY(launch_truemask(c, L, xin, B, mask, nullptr));
+    PI_TRY(launch_truemask(c, L, xin, B, mask, nullptr, true));
   }
-  PI_TRY(launch_up<true>(c, L, x_cur, B, nullptr, nullptr, idx, n, n_log));
-  PI_TRY(launch_down_reduce(c, L, B, idx, n, y));
-  return PI_OK;
+  return launch_down<true>(c, L, B, nullptr, nullptr, y, idx, n, n_log);
 }
 
 }  // namespace
@@ -412,7 +432,7 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   const size_t o_idx = off; off += al(F * 4);
   const size_t o_n = off; off += al(16 * 4);
   const size_t o_a = off; off += al(B * F * 4);
-  const size_t o_part = off; off += al((size_t)G_MAX * B * D * 4);
+  const size_t o_part = off; off += al((size_t)DOWN_G * B * D * 4);
   const size_t o_y = off; off += al(B * D * 4);
   const size_t o_x0 = off; off += al(B * D * 4);
   const size_t o_x1 = off; off += al(B * D * 4);
@@ -479,7 +499,7 @@ pi_status pi_ffn_create(pi_ctx* ctx, const pi_ffn_desc* desc, pi_ffn** out) {
   if (d.d < 8 || d.d % 8) return fail(ctx, PI_ERR_INVALID, "d must be a positive multiple of 8 (got %d)", d.d);
   if (d.ffn < 64 || d.ffn % 64) return fail(ctx, PI_ERR_INVALID, "ffn must be a positive multiple of 64 (got %d)", d.ffn);
   if (d.rank < 0 || d.rank % 8) return fail(ctx, PI_ERR_INVALID, "rank must be 0 or a multiple of 8 (got %d)", d.rank);
-  if (d.rank > 2048) return fail(ctx, PI_ERR_UNSUPPORTED, "rank %d above 2048", d.rank);
+  if (d.rank > 1024) return fail(ctx, PI_ERR_UNSUPPORTED, "rank %d above 1024", d.rank);
   if (d.d > ctx->max_d || d.ffn > ctx->max_ffn || d.rank > ctx->max_rank)
     return fail(ctx, PI_ERR_INVALID, "layer %dx%d rank %d exceeds the context (%dx%d rank %d)", d.d, d.ffn, d.rank,
                 ctx->max_d, ctx->max_ffn, ctx->max_rank);
@@ -528,9 +548,9 @@ pi_status pi_predict(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, u
   const XIn xin{x, nullptr, nullptr};
   if (L.rank > 0) {
     PI_TRY(launch_stage1(ctx, L, xin, B));
-    PI_TRY(launch_stage2(ctx, L, B, mask, logits_out));
+    PI_TRY(launch_stage2(ctx, L, B, mask, logits_out, nullptr));
   } else {
-    PI_TRY(launch_truemask(ctx, L, xin, B, mask, logits_out));
+    PI_TRY(launch_truemask(ctx, L, xin, B, mask, logits_out, false));
   }
   return launch_compact(ctx, L.ffn, idx, n_active);
 }
@@ -546,8 +566,8 @@ pi_status pi_sparse_ffn(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B
   PI_TRY(check_dev_ptr(ctx, y, "y"));
   PI_HIP(ctx, hipSetDevice(ctx->device));
   const LayerDev L = to_dev(ffn->desc);
-  PI_TRY(launch_up<false>(ctx, L, x, B, idx, n_active, nullptr, nullptr, nullptr));
-  return launch_down_reduce(ctx, L, B, idx, n_active, y);
+  PI_TRY(launch_up(ctx, L, x, B, idx, n_active));
+  return launch_down<false>(ctx, L, B, idx, n_active, y, nullptr, nullptr, nullptr);
 }
 
 pi_status pi_layer(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, float* y, uint64_t* mask, int32_t* idx,

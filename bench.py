@@ -86,14 +86,16 @@ def kernel_bytes(cls, L, B, n_list):
     k_up = 1 if L.act == "relu" else 2
     if cls == "stage1":
         return len(n_list) * (r * d * 2 + B * d * xe + B * r * 4)
-    if cls == "stage2":
-        return len(n_list) * (F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8)
-    if cls == "truemask":
-        return len(n_list) * (F * d * w + F * 4 + B * d * xe + (B + 1) * F / 8)
+    up_rows = lambda n: n * (k_up * d * w + 4 + 4 * B)  # noqa: E731  (rows, bias, a written)
+    if cls == "stage2":  # predictor stage 2 + threshold + own active neurons' up (gate) rows
+        return sum(F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8 + B * d * xe + up_rows(n) for n in n_list)
+    if cls == "truemask":  # threshold GEMV + (ReGLU) own active neurons' up rows
+        extra = (lambda n: up_rows(n)) if L.act == "reglu" else (lambda n: n * 4 * B)  # noqa: E731
+        return sum(F * d * w + F * 4 + B * d * xe + (B + 1) * F / 8 + extra(n) for n in n_list)
     if cls == "up":
-        return sum(n * (k_up * d * w + 4 + 4 + 4 * B) + F / 8 + B * d * xe for n in n_list)
-    if cls == "down":
-        return sum(n * (d * w + 4 + 4 * B) + B * d * 4 for n in n_list)
+        return sum(up_rows(n) + 4 * n + B * d * xe for n in n_list)
+    if cls == "down":  # active down rows, their a and the index list (partial sums are overhead)
+        return sum(n * (d * w + 4 + 4 * B) + (B + 1) * F / 8 for n in n_list)
     raise KeyError(cls)
 
 
@@ -107,7 +109,7 @@ def step_bytes(layers, B, nlog_rows):
                 total += kernel_bytes("stage1", L, B, [n]) + kernel_bytes("stage2", L, B, [n])
             else:
                 total += kernel_bytes("truemask", L, B, [n])
-            total += kernel_bytes("up", L, B, [n]) + kernel_bytes("down", L, B, [n])
+            total += kernel_bytes("down", L, B, [n])
     return total
 
 
@@ -201,7 +203,7 @@ def main():
     prof = pi.stack_profile(ctx, ffns, xt[:ps * B].contiguous(), B, yp, nprof)
     npl = nprof.cpu().numpy()
     kb = {}
-    for cls in ("stage1", "stage2", "truemask", "up", "down"):
+    for cls in ("stage1", "stage2", "truemask", "down"):
         tot = 0.0
         for li, L in enumerate(layers):
             if (cls in ("stage1", "stage2") and L.rank == 0) or (cls == "truemask" and L.rank > 0):

@@ -59,7 +59,7 @@ typedef struct pi_ffn pi_ffn;
  * so an active neuron's weights are contiguous rows (P3 «Operator yang Sadar Neuron»).
  *   d        model width, multiple of 8 (of 32 for Q4_0)
  *   ffn      number of FFN neurons, multiple of 64
- *   rank     predictor rank r (multiple of 8, at most 2048; fp16 / Q4_0 layers only), or 0:
+ *   rank     predictor rank r (multiple of 8, at most 1024; fp16 / Q4_0 layers only), or 0:
  *            no predictor, the mask is the true pre-activation of the masked projection
  *            (> threshold)
  *   act      pi_act. ReLU masks the up projection; ReGLU masks the gate.
@@ -153,8 +153,10 @@ pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, cons
                        int32_t T, int32_t B, float *y_out, int32_t *n_active_log, int32_t use_graph);
 
 /* Kernel classes of pi_stack_profile's outputs, in this order:
- * predictor stage 1, predictor stage 2 + threshold, true-mask threshold GEMV, gathered
- * up/gate GEMV (with the index scan), down-projection partials, partial reduction. */
+ * predictor stage 1 (with the glue); predictor stage 2 + threshold + the activations of the
+ * workgroup's own active neurons; true-mask threshold GEMV + activations; gathered up/gate
+ * GEMV of the index-list entry point; down projection into partial sums (with the index
+ * scan); reduction of the partial sums into y. */
 #define PI_KERNEL_CLASSES 6
 
 /* pi_stack_run without a graph, with a hipEvent pair recorded on the context's stream around
