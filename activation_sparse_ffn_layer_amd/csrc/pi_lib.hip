@@ -11,7 +11,7 @@
 #include <vector>
 
 #include "../../include/pi.h"
-#include "pi_kernels.hpp"
+#include "pi_mfma.hpp"
 
 using namespace pi;
 
@@ -34,6 +34,12 @@ struct pi_ctx {
   uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
   uint8_t* xstage = nullptr;    // [max_batch][max_d] fp32-sized
   int32_t* nlog = nullptr;      // [NLOG_CAP]
+  // batched (matrix-core) path
+  float* zpart = nullptr;       // [MM_KS1][max_batch][max_rank]
+  half_t* zhi = nullptr;        // [max_batch][max_rank]
+  half_t* zlo = nullptr;
+  half_t* a16 = nullptr;        // [32 * MT][lda] activations at compacted positions
+  int lda = 0;
   std::string err;
   // cached graph of one stack step, captured on a private stream (the caller's stream may be
   // the null stream, which cannot be captured) and launched on the caller's stream
@@ -284,6 +290,8 @@ pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const in
 // Down projection over the active neurons into DOWN_G partial sums (from the union words,
 // SCAN, which also writes idx and n; or from a given index list), then their reduction into y.
 constexpr int DOWN_G = 16;
+constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
+constexpr int MM_KSD = 16;  // K splits of the batched down projection (<= DOWN_G)
 
 template <int WT, int NB, bool SCAN>
 pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
@@ -346,7 +354,14 @@ pi_status launch_compact(pi_ctx* c, int ffn, int32_t* idx, int32_t* n) {
 pi_status check_batch(pi_ctx* c, const pi_ffn_desc& d, int B) {
   if (B < 1) return fail(c, PI_ERR_INVALID, "B must be >= 1 (got %d)", B);
   if (B > c->max_batch) return fail(c, PI_ERR_INVALID, "B %d exceeds the context's max_batch %d", B, c->max_batch);
-  if (B > 8) return fail(c, PI_ERR_UNSUPPORTED, "batch %d: this build runs batches of 1..8 tokens", B);
+  if (B > 8) {
+    if (B > 64) return fail(c, PI_ERR_UNSUPPORTED, "batch %d: batches run up to 64 tokens", B);
+    if (d.wtype != PI_W_F16)
+      return fail(c, PI_ERR_UNSUPPORTED, "batches above 8 tokens run on fp16 weights (matrix cores)");
+    if (d.d % 16 || d.rank % 16)
+      return fail(c, PI_ERR_UNSUPPORTED, "batches above 8 tokens need d and rank multiples of 16");
+    return PI_OK;
+  }
   if (d.wtype == PI_W_Q4_0 && B > 2)
     return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
   return PI_OK;
@@ -363,6 +378,157 @@ pi_status check_dev_ptr(pi_ctx* c, const void* p, const char* name, bool nullabl
     pi_status s_ = (expr);           \
     if (s_ != PI_OK) return s_;      \
   } while (0)
+
+// ---------------------------------------------------------------- batched path (9..64 tokens)
+
+template <int EPI, int ACT, int MT, bool HILO>
+pi_status launch_mm_rows(pi_ctx* c, const MmRows& p, dim3 grid, int klass) {
+  constexpr int LDR = MM_KW + 8;
+  const size_t lds = (size_t)32 * MT * LDR * 2 * (HILO ? 2 : 1);
+  auto kern = k_mm_rows<EPI, ACT, MT, HILO>;
+  PI_HIP(c, allow_lds(kern, lds));
+  {
+    ProfScope ps(c, klass);
+    hipLaunchKernelGGL(kern, grid, dim3(BLOCK), lds, c->stream, p);
+  }
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+template <int MT>
+pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint32_t* mtok, float* logits) {
+  MmRows p{};
+  p.B = B;
+  p.threshold = L.threshold;
+  p.ffn = L.ffn;
+  if (L.rank > 0) {
+    // stage 1: K-split partial sums of X W1^T, then z as fp16 hi + lo
+    p.x = x;
+    p.K = L.d;
+    p.ldx = L.d;
+    p.w0 = reinterpret_cast<const half_t*>(L.p_w1);
+    p.N = L.rank;
+    const int nt = (L.rank + 127) / 128;
+    int ks = std::max(1, std::min(MM_KS1, 256 / nt));
+    p.ks_len = ((L.d + ks - 1) / ks + MM_KW - 1) / MM_KW * MM_KW;
+    ks = (L.d + p.ks_len - 1) / p.ks_len;
+    p.part = c->zpart;
+    PI_TRY((launch_mm_rows<EPI_PART, ACT_RELU, MT, false>(c, p, dim3(nt, ks), K_STAGE1)));
+    const int BN = B * L.rank;
+    {
+      ProfScope ps(c, K_REDUCE);
+      hipLaunchKernelGGL(k_reduce_hilo, dim3((BN + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, c->stream, c->zpart, ks, BN,
+                         c->zhi, c->zlo);
+    }
+    PI_HIP(c, hipGetLastError());
+    // stage 2: v = Z W2^T + b_p with the mask epilogue
+    MmRows q{};
+    q.x = c->zhi;
+    q.x_lo = c->zlo;
+    q.B = B;
+    q.K = L.rank;
+    q.ldx = L.rank;
+    q.w0 = reinterpret_cast<const half_t*>(L.p_w2);
+    q.N = L.ffn;
+    q.ks_len = L.rank;
+    q.bias = L.p_b;
+    q.threshold = L.threshold;
+    q.mask_tok = mtok;
+    q.mask_union = reinterpret_cast<uint32_t*>(c->munion);
+    q.logits = logits;
+    q.ffn = L.ffn;
+    return launch_mm_rows<EPI_MASK, ACT_RELU, MT, true>(c, q, dim3((L.ffn + 127) / 128, 1), K_STAGE2);
+  }
+  // no predictor: the true pre-activation of the masked projection
+  p.x = x;
+  p.K = L.d;
+  p.ldx = L.d;
+  p.w0 = reinterpret_cast<const half_t*>(L.act == ACT_RELU ? L.w_up : L.w_gate);
+  p.N = L.ffn;
+  p.ks_len = L.d;
+  p.bias = L.b;
+  p.mask_tok = mtok;
+  p.mask_union = reinterpret_cast<uint32_t*>(c->munion);
+  p.logits = logits;
+  return launch_mm_rows<EPI_MASK, ACT_RELU, MT, false>(c, p, dim3((L.ffn + 127) / 128, 1), K_TRUEMASK);
+}
+
+template <int MT>
+pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int32_t* idx, const int32_t* n,
+                 float* y) {
+  MmRows p{};
+  p.x = x;
+  p.B = B;
+  p.K = L.d;
+  p.ldx = L.d;
+  p.w0 = reinterpret_cast<const half_t*>(L.act == ACT_RELU ? L.w_up : L.w_gate);
+  p.w1 = reinterpret_cast<const half_t*>(L.w_up);
+  p.idx = idx;
+  p.n_dev = n;
+  p.ks_len = L.d;
+  p.bias = L.b;
+  p.a16 = c->a16;
+  p.lda = c->lda;
+  p.ffn = L.ffn;
+  const dim3 grid((L.ffn + 127) / 128, 1);
+  if (L.act == ACT_RELU) PI_TRY((launch_mm_rows<EPI_ACT, ACT_RELU, MT, false>(c, p, grid, K_UP)));
+  else PI_TRY((launch_mm_rows<EPI_ACT, ACT_REGLU, MT, false>(c, p, grid, K_UP)));
+  MmDown q{};
+  q.a16 = c->a16;
+  q.lda = c->lda;
+  q.B = B;
+  q.wd = reinterpret_cast<const half_t*>(L.w_down_t);
+  q.idx = idx;
+  q.n_dev = n;
+  q.ffn = L.ffn;
+  q.d = L.d;
+  q.ks_len = ((L.ffn + MM_KSD - 1) / MM_KSD + 15) / 16 * 16;
+  const int ks = (L.ffn + q.ks_len - 1) / q.ks_len;
+  q.part = c->part;
+  {
+    ProfScope ps(c, K_DOWN);
+    hipLaunchKernelGGL(k_mm_down<MT>, dim3((L.d + 511) / 512, ks), dim3(BLOCK), 0, c->stream, q);
+  }
+  PI_HIP(c, hipGetLastError());
+  const int BD = B * L.d;
+  {
+    ProfScope ps(c, K_REDUCE);
+    hipLaunchKernelGGL(k_reduce, dim3((BD + WAVE - 1) / WAVE), dim3(BLOCK), 0, c->stream, c->part, ks, BD, y);
+  }
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+pi_status launch_compact_log(pi_ctx* c, int ffn, int32_t* idx, int32_t* n, int32_t* n_log) {
+  const int W = ffn / 64;
+  {
+    ProfScope ps(c, K_REDUCE);
+    hipLaunchKernelGGL(k_compact, dim3((W + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, c->stream, c->munion, W, idx, n,
+                       n_log);
+  }
+  PI_HIP(c, hipGetLastError());
+  return PI_OK;
+}
+
+pi_status batched_predict(pi_ctx* c, const LayerDev& L, const void* x, int B, uint64_t* mask, float* logits) {
+  uint32_t* mt = reinterpret_cast<uint32_t*>(mask);
+  const half_t* xh = static_cast<const half_t*>(x);
+  return B <= 32 ? mm_predict<1>(c, L, xh, B, mt, logits) : mm_predict<2>(c, L, xh, B, mt, logits);
+}
+
+pi_status batched_ffn(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx, const int32_t* n,
+                      float* y) {
+  const half_t* xh = static_cast<const half_t*>(x);
+  return B <= 32 ? mm_ffn<1>(c, L, xh, B, idx, n, y) : mm_ffn<2>(c, L, xh, B, idx, n, y);
+}
+
+pi_status enqueue_batched(pi_ctx* c, const pi_ffn* f, const void* x, int B, float* y, uint64_t* mask, int32_t* idx,
+                          int32_t* n, int32_t* n_log) {
+  const LayerDev L = to_dev(f->desc);
+  PI_TRY(batched_predict(c, L, x, B, mask, nullptr));
+  PI_TRY(launch_compact_log(c, L.ffn, idx, n, n_log));
+  return batched_ffn(c, L, x, B, idx, n, y);
+}
 
 // Enqueue the whole layer for one batch: three kernels. xin: where x comes from; x_cur: the
 // layer's input in global memory as the activation step reads it (xin.x, or xin.x_out when
@@ -438,6 +604,12 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   const size_t o_x1 = off; off += al(B * D * 4);
   const size_t o_xs = off; off += al(B * D * 4);
   const size_t o_nlog = off; off += al(NLOG_CAP * 4);
+  const bool mm = max_batch > 8;
+  const size_t lda = ((size_t)F + 15) / 16 * 16;
+  const size_t o_zp = off; off += mm ? al((size_t)MM_KS1 * B * R * 4) : 0;
+  const size_t o_zh = off; off += mm ? al(B * R * 2) : 0;
+  const size_t o_zl = off; off += mm ? al(B * R * 2) : 0;
+  const size_t o_a16 = off; off += mm ? al((size_t)(B > 32 ? 64 : 32) * lda * 2) : 0;
   if (hipMalloc(reinterpret_cast<void**>(&c->ws), off) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
@@ -461,6 +633,13 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   c->xbuf[1] = c->ws + o_x1;
   c->xstage = c->ws + o_xs;
   c->nlog = reinterpret_cast<int32_t*>(c->ws + o_nlog);
+  if (mm) {
+    c->zpart = reinterpret_cast<float*>(c->ws + o_zp);
+    c->zhi = reinterpret_cast<half_t*>(c->ws + o_zh);
+    c->zlo = reinterpret_cast<half_t*>(c->ws + o_zl);
+    c->a16 = reinterpret_cast<half_t*>(c->ws + o_a16);
+    c->lda = (int)lda;
+  }
   if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) {
     (void)hipFree(c->ws);
     delete c;
@@ -545,6 +724,10 @@ pi_status pi_predict(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, u
   PI_TRY(check_dev_ptr(ctx, logits_out, "logits_out", true));
   PI_HIP(ctx, hipSetDevice(ctx->device));
   const LayerDev L = to_dev(ffn->desc);
+  if (B > 8) {
+    PI_TRY(batched_predict(ctx, L, x, B, mask, logits_out));
+    return launch_compact(ctx, L.ffn, idx, n_active);
+  }
   const XIn xin{x, nullptr, nullptr};
   if (L.rank > 0) {
     PI_TRY(launch_stage1(ctx, L, xin, B));
@@ -566,6 +749,7 @@ pi_status pi_sparse_ffn(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B
   PI_TRY(check_dev_ptr(ctx, y, "y"));
   PI_HIP(ctx, hipSetDevice(ctx->device));
   const LayerDev L = to_dev(ffn->desc);
+  if (B > 8) return batched_ffn(ctx, L, x, B, idx, n_active, y);
   PI_TRY(launch_up(ctx, L, x, B, idx, n_active));
   return launch_down<false>(ctx, L, B, idx, n_active, y, nullptr, nullptr, nullptr);
 }
@@ -581,6 +765,8 @@ pi_status pi_layer(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, flo
   PI_TRY(check_dev_ptr(ctx, idx, "idx", true));
   PI_TRY(check_dev_ptr(ctx, n_active, "n_active", true));
   PI_HIP(ctx, hipSetDevice(ctx->device));
+  if (B > 8)
+    return enqueue_batched(ctx, ffn, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
   const XIn xin{x, nullptr, nullptr};
   return enqueue_layer(ctx, ffn, xin, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
 }
@@ -675,6 +861,18 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
 
   auto enqueue_step = [&]() -> pi_status {
     for (int l = 0; l < L; ++l) {
+      if (B > 8) {
+        // batched layers take x from global memory: the glue runs as its own kernel
+        const void* x_in = ctx->xstage;
+        if (l > 0) {
+          const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
+          hipLaunchKernelGGL(k_glue<false>, dim3(B), dim3(BLOCK), 0, ctx->stream, ctx->y, x_prev, d, ctx->xbuf[l & 1]);
+          PI_HIP(ctx, hipGetLastError());
+          x_in = ctx->xbuf[l & 1];
+        }
+        PI_TRY(enqueue_batched(ctx, layers[l], x_in, B, ctx->y, nullptr, ctx->idx, ctx->nbuf, ctx->nlog + l));
+        continue;
+      }
       XIn xin;
       const void* x_cur;
       if (l == 0) {

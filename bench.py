@@ -35,10 +35,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128, help="timed steps (tokens at batch 1)")
+    ap.add_argument("--steps", type=int, default=128, help="timed steps (one batch through the stack each)")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="opt6.7b")
-    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=None, help="tokens per step (default: the workload's first batch)")
     ap.add_argument("--layers", type=int, default=None, help="override the stack depth (exploration only)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-steps", type=int, default=16, help="steps of the per-kernel event pass")
@@ -72,6 +72,9 @@ def build_stack(cfg, seed, pi, ctx):
         layers.append(L)
         tables.append(table)
         ffns.append(pi.Ffn(ctx, L, neuron_table=table))
+        if li % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"  generated {li + 1}/{cfg.layers} layers")
     torch.cuda.synchronize()
     return layers, ffns
 
@@ -79,11 +82,24 @@ def build_stack(cfg, seed, pi, ctx):
 def kernel_bytes(cls, L, B, n_list):
     """Algorithmic bytes moved by the launches of one kernel class on one layer.
 
-    n_list: active (union) counts of the launches."""
+    n_list: active (union) counts of the launches. Batches above 8 tokens run the matrix-core
+    path, whose stage-2 and true-mask kernels do not include the activations."""
     w = WBYTES[L.wtype]
     xe = 4 if L.wtype == "f32" else 2
     d, F, r = L.d, L.ffn, L.rank
     k_up = 1 if L.act == "relu" else 2
+    if B > 8:
+        if cls == "stage1":
+            return len(n_list) * (r * d * 2 + B * d * 2 + B * r * 4)
+        if cls == "stage2":
+            return len(n_list) * (F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8)
+        if cls == "truemask":
+            return len(n_list) * (F * d * 2 + F * 4 + B * d * 2 + (B + 1) * F / 8)
+        if cls == "up":
+            return sum(n * (k_up * d * 2 + 4 + 4 + 2 * B) + B * d * 2 for n in n_list)
+        if cls == "down":
+            return sum(n * (d * 2 + 4 + 2 * B) for n in n_list)
+        raise KeyError(cls)
     if cls == "stage1":
         return len(n_list) * (r * d * 2 + B * d * xe + B * r * 4)
     up_rows = lambda n: n * (k_up * d * w + 4 + 4 * B)  # noqa: E731  (rows, bias, a written)
@@ -109,41 +125,40 @@ def step_bytes(layers, B, nlog_rows):
                 total += kernel_bytes("stage1", L, B, [n]) + kernel_bytes("stage2", L, B, [n])
             else:
                 total += kernel_bytes("truemask", L, B, [n])
+            if B > 8:
+                total += kernel_bytes("up", L, B, [n])
             total += kernel_bytes("down", L, B, [n])
     return total
 
 
-def cpu_baseline(cfg, layers, x_tokens, budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample: tokens chained through the stack."""
-    import numpy as np
+def cpu_baseline(cfg, layers, x_tokens, B, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample: one batch of B tokens chained
+    through the stack (union semantics, like the GPU step) until the time budget runs out.
+    Layers are copied to the host one at a time as the oracle reaches them (not timed)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    log(f"cpu baseline: copying {len(layers)} layers to host")
-    hosts = [L.to_host() for L in layers]
-    done_layers = 0
-    tokens = 0
+    x = x_tokens[:B].cpu().numpy()
+    done = 0
     elapsed = 0.0
-    t_all = x_tokens.cpu().numpy()
-    while elapsed < budget_s and tokens < t_all.shape[0]:
-        x = t_all[tokens:tokens + 1]
-        for H in hosts:
-            t0 = time.perf_counter()
-            r = oracle.layer_forward(H, x)
-            x = oracle.glue(r["y"], x)
-            elapsed += time.perf_counter() - t0
-            done_layers += 1
-            if elapsed >= budget_s and done_layers % len(hosts):
-                break
-        tokens += 1
-    token_equiv = done_layers / len(hosts)
-    return {"value": token_equiv / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done_layers} layer passes ({token_equiv:.2f} tokens through the {len(hosts)}-layer stack, "
-                      f"batch 1, chained by the glue) in {elapsed:.1f} s of fp64 numpy compute; weight copies "
-                      f"to host not timed"}
+    for L in layers:
+        H = L.to_host()
+        t0 = time.perf_counter()
+        r = oracle.layer_forward(H, x)
+        x = oracle.glue(r["y"], x)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        del H
+        if elapsed >= budget_s:
+            break
+    frac = done / len(layers)
+    return {"value": B * frac / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one batch of {B} token(s) through {done} of the {len(layers)} layers "
+                      f"({frac:.3f} of a step) in {elapsed:.1f} s of fp64 numpy compute, scaled to a whole "
+                      f"step; weight copies to host not timed"}
 
 
 def main():
@@ -158,7 +173,7 @@ def main():
     cfg = CONFIGS[args.config]
     if args.layers:
         cfg = dataclasses.replace(cfg, layers=args.layers)
-    B = args.batch
+    B = args.batch if args.batch else cfg.batches[0]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     max_rank = max(cfg.layer_rank(0.2), 8)
@@ -203,7 +218,9 @@ def main():
     prof = pi.stack_profile(ctx, ffns, xt[:ps * B].contiguous(), B, yp, nprof)
     npl = nprof.cpu().numpy()
     kb = {}
-    for cls in ("stage1", "stage2", "truemask", "down"):
+    for cls in ("stage1", "stage2", "truemask", "up", "down"):
+        if cls == "up" and B <= 8:
+            continue
         tot = 0.0
         for li, L in enumerate(layers):
             if (cls in ("stage1", "stage2") and L.rank == 0) or (cls == "truemask" and L.rank > 0):
@@ -225,14 +242,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, layers, xt[:B], args.cpu_seconds)
+        cpu = cpu_baseline(cfg, layers, xt, B, args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": {"f16": "f16", "f32": "f32", "q4_0": "q4_0+f16"}[cfg.wtype],
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-shaped {cfg.act} FFN stack", "layers": cfg.layers, "d": cfg.d,
+        "config": {"workload": f"{cfg.name}-shaped {cfg.act} FFN stack, batch {B}", "layers": cfg.layers, "d": cfg.d,
                    "ffn": cfg.ffn, "rank": cfg.rank, "weights": cfg.wtype, "batch": B, "seed": args.seed,
                    "hot_first": cfg.hot_first, "graph": use_graph},
         "hbm_frac_active": round(frac_active, 4),

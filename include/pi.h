@@ -113,7 +113,9 @@ void pi_ffn_destroy(pi_ffn *ffn);
  *             list when B == 1); entries at and beyond n_active are unspecified
  *   n_active  device int32 scalar: length of idx
  *   logits_out nullable fp32 [B][ffn]: the decision values themselves (for checking)
- *   B         1..max_batch; 1..8 run on the vector units, 16..max_batch on matrix cores */
+ *   B         1..max_batch (at most 64); 1..8 run on the vector units (Q4_0: 1..2), 9..64 on the
+ *             matrix cores (fp16 weights, d and rank multiples of 16); mask words are then
+ *             written as 32-bit halves (same bit layout) */
 pi_status pi_predict(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, uint64_t *mask,
                      int32_t *idx, int32_t *n_active, float *logits_out);
 

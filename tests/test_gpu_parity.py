@@ -92,6 +92,11 @@ CASES = {
     "f16-b8": (_cfg("opt6.7b", d=2048, ffn=8192, rank=1024), 1, 16, 8),
     "reglu-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 1, 8, 8),
     "f32-b3": (_cfg("tiny"), 0, 9, 3),
+    # batched path on the matrix cores (9..64 tokens)
+    "relu-b16-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 32, 16),
+    "reglu-b64-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 2, 64, 64),
+    "reglu-b40-truemask-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 3, 40, 40),
+    "llama-full-b64-mfma": (_cfg("llama70b"), 1, 64, 64),
 }
 
 
@@ -102,7 +107,7 @@ def test_layer_parity(case):
     L = make_layer(cfg, li, device="cuda")
     H = L.to_host()
     X = make_tokens(cfg, T, device="cuda", stream=li + 1)
-    ctx = make_ctx([L], max_batch=8)
+    ctx = make_ctx([L], max_batch=max(8, B))
     ffn = pi.Ffn(ctx, L)
     bands = flips = 0
     for s in range(T // B):
@@ -286,9 +291,30 @@ def test_invalid_arguments_enqueue_nothing():
     bad = dataclasses.replace(L, ffn=2000)
     with pytest.raises(pi.PiError, match="multiple of 64"):
         pi.Ffn(ctx, bad)
-    big = pi.Context(max_batch=16, max_d=1024, max_ffn=2048, max_rank=512)
+    big = pi.Context(max_batch=80, max_d=1024, max_ffn=2048, max_rank=512)
     f2 = pi.Ffn(big, L)
-    x16 = make_tokens(cfg, 16, device="cuda")
-    y16 = torch.empty((16, cfg.d), dtype=torch.float32, device="cuda")
+    x70 = make_tokens(cfg, 70, device="cuda")
+    y70 = torch.empty((70, cfg.d), dtype=torch.float32, device="cuda")
     with pytest.raises(pi.PiError, match="unsupported"):
-        pi.layer(big, f2, x16[:12].contiguous(), y16[:12])
+        pi.layer(big, f2, x70, y70)                    # above the 64-token batched path
+    q4 = dataclasses.replace(CONFIGS["opt175b"], d=1024, ffn=2048, rank=512)
+    Lq = make_layer(q4, 0, device="cuda")
+    fq = pi.Ffn(big, Lq)
+    with pytest.raises(pi.PiError, match="unsupported"):
+        pi.layer(big, fq, x70[:4].contiguous(), y70[:4])  # Q4_0 above 2 tokens
+
+
+def test_stack_batched_graph_equals_eager():
+    cfg = _cfg("llama70b", layers=3, d=1024, ffn=4096, rank=512)
+    layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
+    X = make_tokens(cfg, 32, device="cuda")
+    ctx = make_ctx(layers, max_batch=16)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+    outs = []
+    for use_graph in (True, False):
+        y = torch.empty((32, cfg.d), dtype=torch.float32, device="cuda")
+        pi.stack_run(ctx, ffns, X, 16, y, None, use_graph=use_graph)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.all(torch.isfinite(outs[0]))
