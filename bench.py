@@ -14,6 +14,8 @@ MI355X's 8 TB/s), and the fp64 CPU oracle timed on a bounded sample of the same 
 """
 import argparse
 import dataclasses
+import glob
+import hashlib
 import json
 import math
 import os
@@ -26,6 +28,8 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-FFN tokens/s at batch 1 (layer stack) + % of HBM peak on active bytes"
 HBM_PEAK_GBS = 8000.0
 WBYTES = {"f32": 4.0, "f16": 2.0, "q4_0": 18.0 / 32.0}
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+COPY_CAL_BYTES = 1 << 30
 
 
 def log(*a):
@@ -45,7 +49,50 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (3 times), the reference for HBM counters")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; a recorded counter reading is used only while it matches."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "activation_sparse_ffn_layer_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the FETCH_SIZE/WRITE_SIZE table
+    in profiles/, scaled by the plain-copy calibration; None when absent or taken on other
+    kernel sources."""
+    try:
+        with open(TRAFFIC_TABLE, encoding="utf-8") as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    src = kernel_source_hash()
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 8 and cells[0] == workload and cells[1] == kernel and cells[2] == src:
+            try:
+                return float(cells[7])
+            except ValueError:
+                return None
+    return None
+
+
+def calibrate_copy():
+    """A device-to-device copy of exactly 1 GiB, three times: reads and writes 1 GiB each."""
+    import torch
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {COPY_CAL_BYTES} bytes 3 times")
 
 
 def build_stack(cfg, seed, pi, ctx):
@@ -166,6 +213,9 @@ def main():
     if args.gpus != 1:
         log(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).")
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
     import activation_sparse_ffn_layer_amd as pi
     from synth import CONFIGS, make_tokens
@@ -236,8 +286,11 @@ def main():
     dms, dcnt = prof[dom]
     bytes_per_launch = kb[dom] / dcnt
     achieved = bytes_per_launch / (dms / dcnt * 1e-3) / 1e9
+    workload_key = f"{cfg.name} b{B}"
+    traffic = recorded_traffic(workload_key, dom)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "bytes_per_launch": round(bytes_per_launch), "avg_launch_us": round(1e3 * dms / dcnt, 3)}
 
     cpu = None
