@@ -146,19 +146,18 @@ __device__ __forceinline__ uint32_t q4_pair(uint32_t nib, uint32_t sel) {
 constexpr uint32_t SEL_B01 = 0x04010400u;  // bytes 0,1 -> halves (lo, hi)
 constexpr uint32_t SEL_B23 = 0x04030402u;  // bytes 2,3
 
-// sum_e (q_e - 8) * x_e over one block, fp32 accumulate. `xb` = the block's 32 fp16 x values
-// as 16 dwords (dword m holds elements 2m, 2m+1).
-__device__ __forceinline__ float q4_block_dot(u32x4 codes, const uint32_t (&xb)[16], float acc) {
+// The block's (q_e - 8) as 16 fp16 pairs in element order: dword m holds elements 2m, 2m+1.
+// A block's dot product with x is then sum_m dot2(out[m], x pair m), exact products.
+__device__ __forceinline__ void q4_block_unpack(u32x4 codes, uint32_t (&out)[16]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t u = codes[j];
     const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
-    acc = dot2(q4_pair(lo, SEL_B01), xb[2 * j], acc);
-    acc = dot2(q4_pair(lo, SEL_B23), xb[2 * j + 1], acc);
-    acc = dot2(q4_pair(hi, SEL_B01), xb[8 + 2 * j], acc);
-    acc = dot2(q4_pair(hi, SEL_B23), xb[8 + 2 * j + 1], acc);
+    out[2 * j] = q4_pair(lo, SEL_B01);
+    out[2 * j + 1] = q4_pair(lo, SEL_B23);
+    out[8 + 2 * j] = q4_pair(hi, SEL_B01);
+    out[8 + 2 * j + 1] = q4_pair(hi, SEL_B23);
   }
-  return acc;
 }
 
 // Codes of a block as 32 floats in element order (element e = q_e, not yet offset).

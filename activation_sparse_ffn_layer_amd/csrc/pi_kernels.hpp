@@ -3,18 +3,19 @@
 // One layer, one batch of B <= 8 tokens, three dependent kernels:
 //   k_stage1     z = W1 x                 predictor stage 1; when layers are chained, the
 //                                         glue x = fp16(y_prev / rms(y_prev)) is its prologue
-//   k_stage2     v = W2 z + b_p           predictor stage 2 and threshold: a wavefront ballot of
-//                                         (v > th) is the 64-neuron mask word of the workgroup;
-//                                         then the workgroup's own active neurons' up (and gate)
+//   k_stage2     v = W2 z + b_p           predictor stage 2 and threshold: each wave ballots
+//                                         (v > th) over its 8 rows, one byte of the mask word;
+//                                         then the workgroup's active neurons' up (and gate)
 //                                         rows give a_i = act(row_i . x)      [UP variant]
 //   k_truemask   v = W x + b              instead of the two stages when there is no predictor;
 //                                         for ReLU, a_i = max(v_i, 0) comes for free
-//   k_down_cols  y[:, cols] = sum over active i of a_i w_down_t[i][cols]: every workgroup
-//                                         prefix-scans the mask words itself (no waiting on other
-//                                         workgroups), then owns a narrow column slice across
-//                                         all active neurons; no partial sums, deterministic
-// plus k_up (the index-list entry point's gathered GEMV), k_compact, k_threshold, k_glue and
-// k_permute_rows.
+//   k_down_part  y = sum over active i of a_i w_down_t[i]: every workgroup prefix-scans the
+//                                         mask words itself (no waiting on other workgroups),
+//                                         takes one group of active neurons over one column
+//                                         slice into a partial sum; the last workgroup of a
+//                                         slice adds the partials in a fixed order
+// plus k_up (the index-list entry point's gathered GEMV), k_compact, k_threshold, k_glue,
+// k_reduce (partials of the batched path) and k_permute_rows.
 //
 // Pages: P3 = "PowerInfer: Mesin Inferensi LLM Cepat dengan GPU Konsumen" (unite.ai),
 // P1 = "Tüketici sınıfı GPU takılı PC'lerde yüksek hızlı büyük dil modeli serving".
@@ -40,24 +41,50 @@ struct LayerDev {
 //  y == nullptr: x is given ([B][d], fp16 or fp32 storage).
 //  y != nullptr: glue between stacked layers, x = round(y / sqrt(mean(y^2))) per token, or
 //                x_prev (= x) unchanged when y is all zero; workgroup 0 stores it to x_out.
+//                y is the sum of ny partial sums y[g * ystride + t * d + c] (ny >= 1), added
+//                in order g = 0, 1, ... (the previous layer's down projection leaves them).
 struct XIn {
   const void* x;
   const float* y;
   void* x_out;
+  int ny;
+  int ystride;
 };
+
+// Element (t, c) of the glue's y, its partial sums added in order.
+__device__ __forceinline__ float y_at(const XIn& in, size_t tc) {
+  float v = in.y[tc];
+  for (int g = 1; g < in.ny; ++g) v += in.y[(size_t)g * in.ystride + tc];
+  return v;
+}
+// Four consecutive elements of y from (t, c), c % 4 == 0.
+__device__ __forceinline__ u32x4 y4_at(const XIn& in, size_t tc) {
+  constexpr int GU = 8;
+  f32x4 v = __builtin_bit_cast(f32x4, ld16(in.y + tc));
+  for (int g0 = 1; g0 < in.ny; g0 += GU) {
+    u32x4 p[GU];
+#pragma unroll
+    for (int j = 0; j < GU; ++j)
+      p[j] = (g0 + j < in.ny) ? ld16(in.y + (size_t)(g0 + j) * in.ystride + tc) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < GU; ++j)
+      if (g0 + j < in.ny) v += __builtin_bit_cast(f32x4, p[j]);
+  }
+  return __builtin_bit_cast(u32x4, v);
+}
 
 template <bool XF32> struct XType { typedef half_t T; };
 template <> struct XType<true> { typedef float T; };
 
 // Per-token rms of y (0 for an all-zero y) into rms_s[NB].
 template <int NB>
-__device__ void glue_rms(const float* y, int B, int d, float* rms_s, float* red) {
+__device__ void glue_rms(const XIn& in, int B, int d, float* rms_s, float* red) {
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     float ss = 0.f;
     if (t < B)
       for (int c = threadIdx.x * 4; c < d; c += BLOCK * 4) {
-        const u32x4 v = ld16(y + (size_t)t * d + c);
+        const u32x4 v = y4_at(in, (size_t)t * d + c);
         ss = fmaf(u2f(v[0]), u2f(v[0]), ss);
         ss = fmaf(u2f(v[1]), u2f(v[1]), ss);
         ss = fmaf(u2f(v[2]), u2f(v[2]), ss);
@@ -67,6 +94,83 @@ __device__ void glue_rms(const float* y, int B, int d, float* rms_s, float* red)
     if (threadIdx.x == 0) rms_s[t] = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
   }
   __syncthreads();
+}
+
+// Whole-width glue into LDS: xs[t][c] = round(y[t][c] / rms(y[t])) for c < d (x_prev[t][c]
+// when y[t] is all zero), rows t >= B zeroed; also stored to x_out when store_out. Every
+// 16-byte load of a token's y is issued before the first is used (d <= 4 * BLOCK * J;
+// d % 4 == 0). Same summation order as glue_rms.
+constexpr int GLUE_J = 16;
+constexpr int GLUE_NY = 8;  // partial sums the whole-width glue takes (more go through y4_at)
+template <int NB, typename XT, int J = GLUE_J>
+__device__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red, bool store_out) {
+  const int n4 = d >> 2;
+  for (int t = 0; t < NB; ++t) {
+    if (t >= B) {
+      for (int c = threadIdx.x; c < d; c += BLOCK) xs[t * ldx + c] = (XT)0.f;
+      continue;
+    }
+    u32x4 v[J];
+    if (in.ny == 1) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = threadIdx.x + BLOCK * j;
+        v[j] = (c < n4) ? ld16(in.y + (size_t)t * d + 4 * c) : (u32x4){0, 0, 0, 0};
+      }
+    } else {
+      // partial sums: four chunks at a time with all of their (up to GLUE_NY) partials in
+      // flight, added in partial order
+#pragma unroll
+      for (int j0 = 0; j0 < J; j0 += 4) {
+        if (BLOCK * j0 < n4) {
+          u32x4 p[4][GLUE_NY];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < GLUE_NY; ++g) {
+              const int c = threadIdx.x + BLOCK * (j0 + j);
+              p[j][g] = (c < n4 && g < in.ny) ? ld16(in.y + (size_t)g * in.ystride + (size_t)t * d + 4 * c)
+                                              : (u32x4){0, 0, 0, 0};
+            }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4 acc = __builtin_bit_cast(f32x4, p[j][0]);
+#pragma unroll
+            for (int g = 1; g < GLUE_NY; ++g)
+              if (g < in.ny) acc += __builtin_bit_cast(f32x4, p[j][g]);
+            v[j0 + j] = __builtin_bit_cast(u32x4, acc);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j0 + j] = (u32x4){0, 0, 0, 0};
+        }
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      ss = fmaf(u2f(v[j][0]), u2f(v[j][0]), ss);
+      ss = fmaf(u2f(v[j][1]), u2f(v[j][1]), ss);
+      ss = fmaf(u2f(v[j][2]), u2f(v[j][2]), ss);
+      ss = fmaf(u2f(v[j][3]), u2f(v[j][3]), ss);
+    }
+    ss = block_sum(ss, red);
+    const float r = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
+    const XT* xp = reinterpret_cast<const XT*>(in.x) + (size_t)t * d;
+    XT* xo = reinterpret_cast<XT*>(in.x_out) + (size_t)t * d;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = threadIdx.x + BLOCK * j;
+      if (c < n4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const XT o = (r == 0.f) ? xp[4 * c + e] : (XT)(u2f(v[j][e]) / r);
+          xs[t * ldx + 4 * c + e] = o;
+          if (store_out) xo[4 * c + e] = o;
+        }
+      }
+    }
+  }
 }
 
 // Stage x[:, c0 : c0+cw) of NB tokens into LDS xs[t][0..cw) (zeros for t >= B).
@@ -82,7 +186,7 @@ __device__ void stage_x(const XIn& in, int B, int d, int c0, int cw, typename XT
         if (in.y != nullptr) {
           const float r = rms_s[t];
           if (r == 0.f) v = reinterpret_cast<const XT*>(in.x)[gi];
-          else v = (XT)(in.y[gi] / r);
+          else v = (XT)(y_at(in, gi) / r);
           if (store_out) reinterpret_cast<XT*>(in.x_out)[gi] = v;
         } else {
           v = reinterpret_cast<const XT*>(in.x)[gi];
@@ -109,17 +213,17 @@ __device__ void load_x(const void* x, int B, int d, XT* xs) {
 
 // ---------------------------------------------------------------------------------------
 // Partial dot products of R weight rows with NB vectors staged in LDS. Lane l handles each
-// row's 16-byte chunks l, l+64, l+128, ...; the loads of all R rows are issued together.
-// The caller reduces across lanes.
+// row's 16-byte chunks l, l+64, l+128, ...; U chunks of all R rows are in flight at a time.
+// acc may have more rows (RA) than are used. The caller reduces across lanes.
 //   F32: chunk = 4 floats, x fp32.  F16: chunk = 8 halves, x fp16 (dot2).
 //   Q4:  chunk = one 32-element block (16 code bytes + an fp16 scale), x fp16.
 // ---------------------------------------------------------------------------------------
-template <int WT, int NB, int R, typename XT>
-__device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[R], const uint16_t* const (&srow)[R],
-                                         const XT* xs, int ldx, int d, int lane, float (&acc)[R][NB]) {
+template <int WT, int NB, int R, int U, typename XT, int RA>
+__device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[RA], const uint16_t* const (&srow)[RA],
+                                         const XT* xs, int ldx, int d, int lane, float (&acc)[RA][NB]) {
+  static_assert(R <= RA, "more rows than accumulators");
   if constexpr (WT == W_F16 || WT == W_F32) {
     constexpr int EPC = (WT == W_F16) ? 8 : 4;  // elements per 16-byte chunk
-    constexpr int U = (R == 1) ? 8 : 4;
     const int nch = d / EPC;
     for (int c0 = 0; c0 < nch; c0 += WAVE * U) {
       u32x4 w[R][U];
@@ -157,8 +261,7 @@ __device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[R], const u
         }
       }
     }
-  } else {  // W_Q4
-    constexpr int U = (R == 1) ? 4 : 2;
+  } else {  // W_Q4: a lane takes whole blocks, unpacked once for all tokens
     const int nb = d >> 5;
     for (int c0 = 0; c0 < nb; c0 += WAVE * U) {
       u32x4 w[R][U];
@@ -175,6 +278,10 @@ __device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[R], const u
       for (int u = 0; u < U; ++u) {
         const int c = c0 + lane + WAVE * u;
         if (c < nb) {
+          // (q - 8) of every row's block as fp16 pairs, once for all tokens
+          uint32_t wq[R][16];
+#pragma unroll
+          for (int q = 0; q < R; ++q) q4_block_unpack(w[q][u], wq[q]);
 #pragma unroll
           for (int t = 0; t < NB; ++t) {
             const half_t* xb = reinterpret_cast<const half_t*>(xs) + t * ldx + c * 32;
@@ -188,7 +295,12 @@ __device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[R], const u
               xv[4 * m + 3] = qv[3];
             }
 #pragma unroll
-            for (int q = 0; q < R; ++q) acc[q][t] = fmaf(sc[q][u], q4_block_dot(w[q][u], xv, 0.f), acc[q][t]);
+            for (int q = 0; q < R; ++q) {
+              float s = 0.f;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) s = dot2(wq[q][e], xv[e], s);
+              acc[q][t] = fmaf(sc[q][u], s, acc[q][t]);
+            }
           }
         }
       }
@@ -207,75 +319,154 @@ __device__ __forceinline__ const uint16_t* scale_ptr(const uint16_t* base, int i
   return (WT == W_Q4) ? base + (size_t)i * (d >> 5) : nullptr;
 }
 
-// a[t][i] = act(...) for the listed neurons of one wave, two rows in flight at a time:
-// ReLU pairs two neurons (up rows), ReGLU takes one neuron's gate and up rows together.
-template <int WT, int ACT, int NB, typename XT>
-__device__ __forceinline__ void act_pair(const LayerDev& L, const XT* xs, int B, int lane, int i0, int i1,
-                                         float* __restrict__ a) {
-  const int d = L.d, ffn = L.ffn;
-  if constexpr (ACT == ACT_RELU) {
-    const int j1 = (i1 >= 0) ? i1 : i0;
-    const uint8_t* const rows[2] = {row_ptr<WT>(L.w_up, i0, d), row_ptr<WT>(L.w_up, j1, d)};
-    const uint16_t* const srows[2] = {scale_ptr<WT>(L.s_up, i0, d), scale_ptr<WT>(L.s_up, j1, d)};
-    float acc[2][NB] = {};
-    rows_dot<WT, NB, 2, XT>(rows, srows, xs, d, d, lane, acc);
-    const float b0 = L.b[i0], b1 = L.b[j1];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const float h0 = wave_sum(acc[0][t]) + b0;
-      const float h1 = wave_sum(acc[1][t]) + b1;
-      if (lane == t && t < B) {
-        a[(size_t)t * ffn + i0] = fmaxf(h0, 0.f);
-        if (i1 >= 0) a[(size_t)t * ffn + i1] = fmaxf(h1, 0.f);
-      }
-    }
-  } else {
-    const uint8_t* const rows[2] = {row_ptr<WT>(L.w_gate, i0, d), row_ptr<WT>(L.w_up, i0, d)};
-    const uint16_t* const srows[2] = {scale_ptr<WT>(L.s_gate, i0, d), scale_ptr<WT>(L.s_up, i0, d)};
-    float acc[2][NB] = {};
-    rows_dot<WT, NB, 2, XT>(rows, srows, xs, d, d, lane, acc);
-    const float b0 = L.b[i0];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const float g = wave_sum(acc[0][t]) + b0;
-      const float u = wave_sum(acc[1][t]);
-      if (lane == t && t < B) a[(size_t)t * ffn + i0] = fmaxf(g, 0.f) * u;
-    }
-  }
+// ---------------------------------------------------------------------------------------
+// Activation rounds. A workgroup computes a_i for a list of `cnt` neurons (item k is neuron
+// id_of(k)); item k goes to wave k % 4, and in each round a wave takes up to PW of its items
+// (ReLU: PW = 4 up rows; ReGLU: PW = 2 neurons = 4 rows, gate and up) with all their rows in
+// flight together. The number of rounds depends only on cnt, so every wave passes the same
+// barriers: x may be staged in column windows of width dw (stage(c0, cw) fills xs) when it
+// does not fit in LDS whole (dw == d: xs already holds x).
+// a_i is computed the same way whichever wave, round or window layout handles it: each lane
+// sums its chunks in ascending order, then the wave sums the lanes.
+// ---------------------------------------------------------------------------------------
+template <int WT>
+__device__ __forceinline__ const uint8_t* row_at(const uint8_t* base, int i, int d, int c0) {
+  if constexpr (WT == W_F32) return base + ((size_t)i * d + c0) * 4;
+  else if constexpr (WT == W_F16) return base + ((size_t)i * d + c0) * 2;
+  else return base + ((size_t)i * (d >> 5) + (c0 >> 5)) * 16;
+}
+template <int WT>
+__device__ __forceinline__ const uint16_t* scale_at(const uint16_t* base, int i, int d, int c0) {
+  if constexpr (WT == W_Q4) return base + (size_t)i * (d >> 5) + (c0 >> 5);
+  else return nullptr;
 }
 
-// The active neurons of a 64-neuron word u (union over the batch), shared out over the 4
-// waves of the workgroup: wave w takes set bits w, w+4, ... (ReLU: two per step).
-template <int WT, int ACT, int NB, typename XT>
-__device__ void word_activations(const LayerDev& L, const XT* xs, int B, int base, uint64_t u, int wave, int lane,
-                                 float* __restrict__ a) {
-  const int cnt = __popcll(u);
-  constexpr int STEP = (ACT == ACT_RELU) ? 2 * NWAVES : NWAVES;
-  for (int r = wave; r < cnt; r += STEP) {
-    const int i0 = base + select_bit(u, r);
-    int i1 = -1;
-    if constexpr (ACT == ACT_RELU)
-      if (r + NWAVES < cnt) i1 = base + select_bit(u, r + NWAVES);
-    act_pair<WT, ACT, NB, XT>(L, xs, B, lane, i0, i1, a);
-  }
-}
+// Chunks per lane in flight per row for R rows in flight: about 128 VGPRs of weights.
+template <int WT, int R> struct ActU {
+  static constexpr int U = (WT == W_Q4) ? 16 / R : (32 / R > 16 ? 16 : 32 / R);
+};
 
-// The active neurons among one wave's rows (bits of `bits`, neuron base + bit), two rows in
-// flight at a time.
-template <int WT, int ACT, int NB, typename XT>
-__device__ void word_activations_wave(const LayerDev& L, const XT* xs, int B, int base, uint32_t bits, int lane,
-                                      float* __restrict__ a) {
-  while (bits) {
-    const int i0 = base + __ffs(bits) - 1;
-    bits &= bits - 1;
-    int i1 = -1;
+constexpr int ACT_RA = 4;  // rows in flight per wave in a round
+template <int ACT> struct ActPW { static constexpr int PW = (ACT == ACT_RELU) ? 4 : 2; };
+
+// acc[r][t] += row_r[c0, c0+cw) . xs[t][0, cw) for the rows of the first NR ids.
+template <int WT, int ACT, int NB, int NR, typename XT>
+__device__ __forceinline__ void act_accum(const LayerDev& L, const XT* xs, int ldx, int c0, int cw, int lane,
+                                          const int (&ids)[ActPW<ACT>::PW], float (&acc)[ACT_RA][NB]) {
+  constexpr int R = (ACT == ACT_RELU ? 1 : 2) * NR;
+  const int d = L.d;
+  const uint8_t* rows[ACT_RA] = {nullptr, nullptr, nullptr, nullptr};
+  const uint16_t* srows[ACT_RA] = {nullptr, nullptr, nullptr, nullptr};
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
     if constexpr (ACT == ACT_RELU) {
-      if (bits) {
-        i1 = base + __ffs(bits) - 1;
-        bits &= bits - 1;
+      rows[q] = row_at<WT>(L.w_up, ids[q], d, c0);
+      srows[q] = scale_at<WT>(L.s_up, ids[q], d, c0);
+    } else {
+      rows[2 * q] = row_at<WT>(L.w_gate, ids[q], d, c0);
+      srows[2 * q] = scale_at<WT>(L.s_gate, ids[q], d, c0);
+      rows[2 * q + 1] = row_at<WT>(L.w_up, ids[q], d, c0);
+      srows[2 * q + 1] = scale_at<WT>(L.s_up, ids[q], d, c0);
+    }
+  }
+  rows_dot<WT, NB, R, ActU<WT, R>::U, XT, ACT_RA>(rows, srows, xs, ldx, cw, lane, acc);
+}
+
+template <int ACT, int NB>
+__device__ __forceinline__ void act_store(const LayerDev& L, int B, int lane, const int (&ids)[ActPW<ACT>::PW], int m,
+                                          float (&acc)[ACT_RA][NB], float* __restrict__ a) {
+  constexpr int PW = ActPW<ACT>::PW;
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    if (q < m) {
+      const float bias = L.b[ids[q]];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        float v;
+        if constexpr (ACT == ACT_RELU) {
+          v = fmaxf(wave_sum(acc[q][t]) + bias, 0.f);
+        } else {
+          const float g = wave_sum(acc[2 * q][t]) + bias;
+          const float u = wave_sum(acc[2 * q + 1][t]);
+          v = fmaxf(g, 0.f) * u;
+        }
+        if (lane == t && t < B) a[(size_t)t * L.ffn + ids[q]] = v;
       }
     }
-    act_pair<WT, ACT, NB, XT>(L, xs, B, lane, i0, i1, a);
+  }
+}
+
+template <int WT, int ACT, int NB, typename XT, typename IdOf, typename Stage>
+__device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const XT* xs, int ldx, int dw, Stage stage,
+                           float* __restrict__ a) {
+  constexpr int PW = ActPW<ACT>::PW;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int d = L.d;
+  const int rounds = (cnt + NWAVES * PW - 1) / (NWAVES * PW);
+  for (int rho = 0; rho < rounds; ++rho) {
+    int ids[PW];
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int k = wave + NWAVES * (rho * PW + j);
+      ids[j] = (k < cnt) ? id_of(k) : 0;
+      m += (k < cnt) ? 1 : 0;
+    }
+    float acc[ACT_RA][NB];
+#pragma unroll
+    for (int q = 0; q < ACT_RA; ++q)
+#pragma unroll
+      for (int t = 0; t < NB; ++t) acc[q][t] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += dw) {
+      const int cw = min(dw, d - c0);
+      if (dw < d) {
+        __syncthreads();
+        stage(c0, cw);
+        __syncthreads();
+      }
+      if constexpr (ACT == ACT_RELU) {
+        switch (m) {
+          case 1: act_accum<WT, ACT, NB, 1, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
+          case 2: act_accum<WT, ACT, NB, 2, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
+          case 3: act_accum<WT, ACT, NB, 3, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
+          case 4: act_accum<WT, ACT, NB, 4, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
+          default: break;
+        }
+      } else {
+        switch (m) {
+          case 1: act_accum<WT, ACT, NB, 1, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
+          case 2: act_accum<WT, ACT, NB, 2, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
+          default: break;
+        }
+      }
+    }
+    act_store<ACT, NB>(L, B, lane, ids, m, acc, a);
+  }
+}
+
+// Copy columns [c0, c0 + cw) of x [NB][d] (rows t >= B zeroed) into xs[t][0, cw) with
+// 16-byte accesses (cw * sizeof(XT) % 16 == 0). The NB x cw/E chunks form one flat range:
+// each thread issues J loads (over all tokens) before storing any.
+template <int NB, typename XT>
+__device__ void load_x_cols(const void* x, int B, int d, int c0, int cw, XT* xs, int ldx) {
+  constexpr int E = 16 / sizeof(XT);
+  constexpr int J = 16;
+  const int n16 = cw / E, total = NB * n16;
+  for (int f0 = 0; f0 < total; f0 += BLOCK * J) {
+    u32x4 v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f = f0 + threadIdx.x + BLOCK * j;
+      const int t = f / n16, c = f - t * n16;
+      v[j] = (f < total && t < B) ? ld16(reinterpret_cast<const XT*>(x) + (size_t)t * d + c0 + c * E)
+                                  : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f = f0 + threadIdx.x + BLOCK * j;
+      const int t = f / n16, c = f - t * n16;
+      if (f < total) *reinterpret_cast<u32x4*>(xs + t * ldx + c * E) = v[j];
+    }
   }
 }
 
@@ -328,14 +519,25 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
     const int c = lane + WAVE * u;
     wp[u] = (row < r && c < nch0) ? ld_stream(wrow0 + (size_t)c * 16) : (u32x4){0, 0, 0, 0};
   }
-  if (xin.y != nullptr) glue_rms<NB>(xin.y, B, d, rms_s, red);
+  // x fits in LDS (and, for the glue, in one pass of registers): glue or copy it at once
+  constexpr int GJ = (NB >= 8) ? 4 : (NB >= 4) ? 8 : GLUE_J;  // x of NB tokens in 64 KB: d <= 4 * BLOCK * GJ
+  const bool whole = dc >= d && (xin.y == nullptr || (d <= 4 * BLOCK * GJ && xin.ny <= GLUE_NY));
+  if (whole) {
+    if (xin.y != nullptr) glue_x<NB, half_t, GJ>(xin, B, d, xs, d, red, blockIdx.x == 0);
+    else load_x_cols<NB, half_t>(xin.x, B, d, 0, d, xs, d);
+  } else if (xin.y != nullptr) {
+    glue_rms<NB>(xin, B, d, rms_s, red);
+  }
   float acc[1][NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) acc[0][t] = 0.f;
   for (int c0 = 0; c0 < d; c0 += dc) {
     const int cw = min(dc, d - c0);
     __syncthreads();
-    stage_x<NB, false>(xin, B, d, c0, cw, xs, dc, rms_s, blockIdx.x == 0);
+    if (!whole) {
+      if (xin.y != nullptr) stage_x<NB, false>(xin, B, d, c0, cw, xs, dc, rms_s, blockIdx.x == 0);
+      else load_x_cols<NB, half_t>(xin.x, B, d, c0, cw, xs, dc);
+    }
     __syncthreads();
     if (row < r) {
       int done = 0;  // chunks of this window already accumulated
@@ -361,7 +563,7 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
       if (done * 8 < cw) {
         const uint8_t* const rows[1] = {wrow0 + ((size_t)c0 + done * 8) * 2};
         const uint16_t* const srows[1] = {nullptr};
-        rows_dot<W_F16, NB, 1, half_t>(rows, srows, xs + done * 8, dc, cw - done * 8, lane, acc);
+        rows_dot<W_F16, NB, 1, 8, half_t, 1>(rows, srows, xs + done * 8, dc, cw - done * 8, lane, acc);
       }
     }
   }
@@ -375,29 +577,31 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
 }
 
 // ---------------------------------------------------------------------------------------
-// k_stage2: v = W2 z + b_p for the TILE neurons of this workgroup (TILE/4 rows per wave, at
-// most 8 so one wave's rows are one byte of the mask), then the threshold: each wave ballots
-// (v > th) over its own rows and stores that byte of the token's and the batch union's 64-bit
-// mask word itself. W2 rows are issued before z is read. Lane l keeps z at chunks l + 64j as
-// two fp16 halves z = hi + lo (hi = fp16(z), lo = fp16(z - hi), together about 22 significant
-// bits), so W2 (fp16) . z runs on dot2 with exact products.
-// UP: each wave then goes straight on to the up (and gate) rows of its own active neurons,
-// without waiting for the rest of the workgroup; a is dense by neuron id ([B][ffn]). x is
-// staged in LDS while the W2 rows are in flight.
+// k_stage2: v = W2 z + b_p and the threshold for 32 neurons per workgroup: wave w owns the 8
+// neurons of mask byte w * gridDim.x + blockIdx.x (bytes are dealt out across workgroups, so a
+// hot-first layout does not load a few workgroups with every active neuron). Each wave ballots
+// (v > th) over its rows and stores that byte of the token's and the batch union's mask words.
+// W2 rows are issued before z is read. Lane l keeps z at chunks l + 64j as two fp16 halves
+// z = hi + lo (hi = fp16(z), lo = fp16(z - hi), together about 22 significant bits), so
+// W2 (fp16) . z runs on dot2 with exact products.
+// UP: then the workgroup's active neurons (up to 32) get their activations in balanced rounds
+// over its 4 waves; a is dense by neuron id ([B][ffn]). x is staged in LDS while the W2 rows
+// are in flight (in column windows of width xw after the threshold when it does not fit).
 // ---------------------------------------------------------------------------------------
-template <int NB, int CPL, int TILE, bool UP, int WT, int ACT>
+template <int NB, int CPL, bool UP, int WT, int ACT>
 __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __restrict__ z, int B,
                                                   uint64_t* __restrict__ mask_tok, uint64_t* __restrict__ mask_union,
-                                                  float* __restrict__ logits, const void* __restrict__ x,
+                                                  float* __restrict__ logits, const void* __restrict__ x, int xw,
                                                   float* __restrict__ a) {
-  constexpr int RPT = TILE / NWAVES;  // rows per wave
-  static_assert(RPT == 8, "a wave owns exactly one byte of the mask");
+  constexpr int RPT = 8;  // rows per wave: one byte of the mask
   typedef typename XType<WT == W_F32>::T XT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
+  __shared__ uint32_t s_bits[NWAVES];
   const int r = L.rank, nch = r >> 3;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int row0 = blockIdx.x * TILE + wave * RPT;  // first neuron of this wave
+  const int byte = wave * gridDim.x + blockIdx.x;  // this wave's byte of the mask
+  const int row0 = byte * RPT;                      // its first neuron
   const uint8_t* w2 = reinterpret_cast<const uint8_t*>(L.p_w2);
   u32x4 w[RPT][CPL];
 #pragma unroll
@@ -429,14 +633,12 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
       }
     }
   if constexpr (UP) {
-    load_x<NB, XT>(x, B, L.d, xs);
-    __syncthreads();
+    if (xw >= L.d) load_x_cols<NB, XT>(x, B, L.d, 0, L.d, xs, L.d);
   }
   const float bias = L.p_b[row0 + (lane & (RPT - 1))];
   uint32_t ubits = 0;
   const int W = L.ffn >> 6;
   uint8_t* mt = reinterpret_cast<uint8_t*>(mask_tok);
-  const int byte = row0 >> 3;  // this wave's byte of the mask
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     float acc[RPT];
@@ -461,7 +663,19 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
     }
   }
   if (lane == 0) reinterpret_cast<uint8_t*>(mask_union)[byte] = (uint8_t)ubits;
-  if constexpr (UP) word_activations_wave<WT, ACT, NB, XT>(L, xs, B, row0, ubits, lane, a);
+  if constexpr (UP) {
+    if (lane == 0) s_bits[wave] = ubits;
+    __syncthreads();
+    const uint32_t cm = s_bits[0] | (s_bits[1] << 8) | (s_bits[2] << 16) | (s_bits[3] << 24);
+    const int g = blockIdx.x, nwg = gridDim.x;
+    auto id_of = [cm, g, nwg](int k) {
+      const int j = select_bit((uint64_t)cm, k);
+      return ((j >> 3) * nwg + g) * RPT + (j & 7);
+    };
+    const int xl = (xw >= L.d) ? L.d : xw;
+    auto stage = [&](int c0, int cw) { load_x_cols<NB, XT>(x, B, L.d, c0, cw, xs, xl); };
+    act_rounds<WT, ACT, NB, XT>(L, B, __popc(cm), id_of, xs, xl, xl, stage, a);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -477,14 +691,13 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
   __shared__ float red[NWAVES];
-  __shared__ float rms_s[NB];
   __shared__ float vs[NB][WAVE];
   __shared__ uint64_t s_union;
   const int d = L.d, ffn = L.ffn;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int tile = blockIdx.x;
-  if (xin.y != nullptr) glue_rms<NB>(xin.y, B, d, rms_s, red);
-  stage_x<NB, XF32>(xin, B, d, 0, d, xs, d, rms_s, blockIdx.x == 0);
+  if (xin.y != nullptr) glue_x<NB, XT>(xin, B, d, xs, d, red, blockIdx.x == 0);
+  else load_x_cols<NB, XT>(xin.x, B, d, 0, d, xs, d);
   __syncthreads();
   const uint8_t* W = (L.act == ACT_RELU) ? L.w_up : L.w_gate;
   const uint16_t* S = (L.act == ACT_RELU) ? L.s_up : L.s_gate;
@@ -495,7 +708,7 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
     const uint8_t* const rows[2] = {row_ptr<WT>(W, row, d), row_ptr<WT>(W, row + 1, d)};
     const uint16_t* const srows[2] = {scale_ptr<WT>(S, row, d), scale_ptr<WT>(S, row + 1, d)};
     float acc[2][NB] = {};
-    rows_dot<WT, NB, 2, XT>(rows, srows, xs, d, d, lane, acc);
+    rows_dot<WT, NB, 2, (WT == W_Q4 ? 2 : 4), XT, 2>(rows, srows, xs, d, d, lane, acc);
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const float v0 = wave_sum(acc[0][t]) + L.b[row];
@@ -523,7 +736,11 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
   if constexpr (UP) {
     if (L.act == ACT_REGLU) {
       __syncthreads();
-      word_activations<WT, ACT_REGLU, NB, XT>(L, xs, B, tile * WAVE, s_union, wave, lane, a);
+      const uint64_t u = s_union;
+      const int base = tile * WAVE;
+      auto id_of = [u, base](int k) { return base + select_bit(u, k); };
+      auto stage = [](int, int) {};
+      act_rounds<WT, ACT_REGLU, NB, XT>(L, B, __popcll(u), id_of, xs, d, d, stage, a);
     }
   }
 }
@@ -561,17 +778,6 @@ __device__ __forceinline__ int scan_words(const uint64_t* __restrict__ words, in
   return carry;
 }
 
-// Neuron id of active position k (< n) from the scanned words.
-__device__ __forceinline__ int neuron_at(const uint64_t* wl, const int* pre, int W, int k) {
-  int lo = 0, hi = W;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= k) lo = mid;
-    else hi = mid;
-  }
-  return lo * WAVE + select_bit(wl[lo], k - pre[lo]);
-}
-
 // ---------------------------------------------------------------------------------------
 // Compaction: ascending indices of the set bits of W union words. Workgroup g writes the
 // indices of words [256g, 256g+256): it counts all earlier set bits itself (no inter-
@@ -605,99 +811,154 @@ __global__ __launch_bounds__(BLOCK) void k_compact(const uint64_t* __restrict__ 
 // ---------------------------------------------------------------------------------------
 // k_up (index-list entry point): a[t][i_k] = act(row_{i_k} . x_t) for k < n, with idx and n
 // given by the caller (n clamped to [0, ffn], entries outside [0, ffn) skipped). a is dense
-// by neuron id. Waves take positions k in turn, two neurons (ReLU) or one (ReGLU) at a time.
+// by neuron id. Workgroup g takes the positions [CH*g, CH*g + CH), [CH*(g + grid), ...) in
+// activation rounds (CH = 4 waves x PW); x is in LDS whole, or staged in column windows of
+// width xw.
 // ---------------------------------------------------------------------------------------
 template <int WT, int ACT, int NB>
-__global__ __launch_bounds__(BLOCK) void k_up(LayerDev L, const void* __restrict__ x, int B,
+__global__ __launch_bounds__(BLOCK) void k_up(LayerDev L, const void* __restrict__ x, int B, int xw,
                                               const int32_t* __restrict__ idx_in, const int32_t* __restrict__ n_in,
                                               float* __restrict__ a) {
   typedef typename XType<WT == W_F32>::T XT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
-  const int ffn = L.ffn;
-  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  __shared__ int s_ids[NWAVES * ActPW<ACT>::PW];
+  __shared__ int s_cnt;
+  constexpr int CH = NWAVES * ActPW<ACT>::PW;
+  const int ffn = L.ffn, d = L.d;
   const int n = min(max(*n_in, 0), ffn);
-  load_x<NB, XT>(x, B, L.d, xs);
-  __syncthreads();
-  const int total_waves = gridDim.x * NWAVES;
-  constexpr int PER = (ACT == ACT_RELU) ? 2 : 1;
-  for (int k = (blockIdx.x * NWAVES + wave) * PER; k < n; k += total_waves * PER) {
-    const int i0 = idx_in[k];
-    int i1 = (PER == 2 && k + 1 < n) ? idx_in[k + 1] : -1;
-    if ((unsigned)i1 >= (unsigned)ffn) i1 = -1;
-    if ((unsigned)i0 >= (unsigned)ffn) {  // a caller-supplied entry out of range: skipped
-      if (i1 >= 0) act_pair<WT, ACT, NB, XT>(L, xs, B, lane, i1, -1, a);
-      continue;
+  const int xl = (xw >= d) ? d : xw;
+  if (xw >= d) load_x_cols<NB, XT>(x, B, d, 0, d, xs, d);
+  auto stage = [&](int c0, int cw) { load_x_cols<NB, XT>(x, B, d, c0, cw, xs, xl); };
+  for (int k0 = blockIdx.x * CH; k0 < n; k0 += gridDim.x * CH) {
+    // this chunk's valid entries, in order
+    __syncthreads();
+    if (threadIdx.x < WAVE) {
+      const int k = k0 + threadIdx.x;
+      const int i = (threadIdx.x < CH && k < n) ? idx_in[k] : -1;
+      const bool ok = (unsigned)i < (unsigned)ffn;
+      const uint64_t bal = __ballot(ok);
+      if (ok) s_ids[__popcll(bal & ((1ull << threadIdx.x) - 1))] = i;
+      if (threadIdx.x == 0) s_cnt = __popcll(bal);
     }
-    act_pair<WT, ACT, NB, XT>(L, xs, B, lane, i0, i1, a);
+    __syncthreads();
+    const int cnt = s_cnt;
+    auto id_of = [](int k) { return s_ids[k]; };
+    act_rounds<WT, ACT, NB, XT>(L, B, cnt, id_of, xs, xl, xl, stage, a);
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_down_part: part[g][t][c] = sum over the active positions k of group g of a[t][i_k] *
-// w_down_t[i_k][c], for the columns c of slice blockIdx.y. The grid is G groups x S slices;
-// group g takes positions k = g, g + G, g + 2G, ... A slice is SEG lanes x 16 bytes of a row
-// (fp16: 8*SEG columns, fp32: 4*SEG, Q4_0: 32*SEG); the workgroup's 256 threads form 256/SEG
-// neuron slots, each with U rows in flight, and the slots are summed in a fixed order. The G
-// partial sums are added later in a fixed order too (by k_reduce, or by the next layer's
-// glue), so y does not depend on scheduling.
-//  SCAN: positions come from the union words: every workgroup prefix-scans them and expands
-//        its own group's positions (k = g + G*j, j < IDX_LDS) into an index list in LDS;
-//        beyond that a position is found by binary search. Workgroup (0, 0) also writes
-//        idx[k] and n. Otherwise idx and n are given.
+// k_down_part: part[g][t][c] = sum over the active neurons i of group g of a[t][i] *
+// w_down_t[i][c]. Group g holds the neurons of mask words w = g, g + G, g + 2G, ... (words
+// dealt out in turn, so a hot-first layout still spreads its hot words over the groups), in
+// ascending order. The grid is G groups x S column slices (block = g + G * s); a slice is
+// SEG lanes of EPC columns each; the workgroup's 256 threads form 256/SEG neuron slots with
+// U rows in flight each, summed in a fixed order. The G partial sums are added later in
+// group order (by k_reduce, or by the next layer's glue), so y does not depend on
+// scheduling. (Adding them here, in the last workgroup of each slice, needs a device-scope
+// release per workgroup: an L2 write-back that costs far more than the separate pass.)
+//  SCAN: the group's neurons come from the union words (no workgroup needs the others'
+//        counts). One extra workgroup (the last block) prefix-scans all the words and writes
+//        the ascending index list idx and n.
+//  else: the given index list, filtered to the group's words in list order (an ascending
+//        list gives the same group lists, hence the same y, as SCAN).
+// Q4_0 (QS lanes per 32-element block): QS = 1: a lane takes a whole block (16 code bytes);
+// QS = 4: a lane takes 4 code bytes, i.e. elements 4j..4j+3 and 16+4j..16+4j+3 of the block.
 // ---------------------------------------------------------------------------------------
-constexpr int IDX_LDS = 2048;  // per-group active positions expanded into LDS by the down kernel
-
-template <int WT> struct DownGeom {
-  static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32;  // columns per 16-byte chunk
-  static constexpr int SEG = (WT == W_Q4) ? 4 : 8;                       // lanes per row segment
-  static constexpr int SW = SEG * EPC;                                   // slice width (columns)
+template <int WT, int QS> struct DownGeom {
+  static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32 / QS;  // columns per lane
+  static constexpr int SEG = (WT == W_Q4) ? 4 * QS : 8;                       // lanes per slice
+  static constexpr int SW = SEG * EPC;                                         // slice width (columns)
 };
 
-template <int WT, int NB, bool SCAN, int SEG, int U, int GC = 0, int XMODE = 0>
+// Column (within the slice) of element e of lane sl.
+template <int WT, int QS>
+__device__ __forceinline__ int down_col(int sl, int e) {
+  if constexpr (WT == W_Q4 && QS == 4) return (sl >> 2) * 32 + 4 * (sl & 3) + (e < 4 ? e : 12 + e);
+  else return sl * DownGeom<WT, QS>::EPC + e;
+}
+
+// Capacity of a group's neuron list (ints in LDS): every neuron of its words.
+__host__ __device__ constexpr int down_list_cap(int W, int G) { return (W + G - 1) / G * 64; }
+
+template <int WT, int NB, bool SCAN, int U, int QS, int G>
 __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const uint64_t* __restrict__ words,
                                                      const int32_t* __restrict__ idx_in,
                                                      const int32_t* __restrict__ n_in, const float* __restrict__ a,
-                                                     float* __restrict__ part, int G, int32_t* __restrict__ idx_out,
+                                                     float* __restrict__ part, int32_t* __restrict__ idx_out,
                                                      int32_t* __restrict__ n_out, int32_t* __restrict__ n_log) {
-  constexpr int EPC = DownGeom<WT>::EPC;
+  static_assert(G >= 1 && (G & (G - 1)) == 0, "the group count is a power of two");
+  constexpr int EPC = DownGeom<WT, QS>::EPC;
+  constexpr int SEG = DownGeom<WT, QS>::SEG;
   constexpr int SW = SEG * EPC;
   constexpr int NSL = BLOCK / SEG;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int red[NWAVES];
   __shared__ float s_red[NSL][SW + 1];
+  __shared__ int s_ng;
   const int d = L.d, ffn = L.ffn, W = ffn >> 6;
-  if constexpr (GC > 0) G = GC;
-  const int g = blockIdx.x, s = blockIdx.y;
-  const int slot = threadIdx.x / SEG, sl = threadIdx.x % SEG;
-  const int col0 = s * SW + sl * EPC;
-  const bool valid = col0 < d;
-  uint64_t* wl = reinterpret_cast<uint64_t*>(smem);
-  int* pre = reinterpret_cast<int*>(wl + W);
-  int* il = pre + W + 1;  // [IDX_LDS] expanded index list
-  int n;
+  int* il = reinterpret_cast<int*>(smem);  // the group's neurons [down_list_cap(W, G)]
   if constexpr (SCAN) {
-    n = scan_words(words, W, wl, pre, red);
-    const bool writer = (XMODE & 1) ? false : (g == 0 && s == 0);
-    for (int w = threadIdx.x; w < W; w += BLOCK) {
-      uint64_t word = wl[w];
-      int pos = pre[w];
-      while (word) {
-        const int i = w * WAVE + __ffsll((unsigned long long)word) - 1;
-        word &= word - 1;
-        if (writer) idx_out[pos] = i;
-        if (pos % G == g && pos / G < IDX_LDS) il[pos / G] = i;
-        ++pos;
+    if (blockIdx.x == gridDim.x - 1) {  // the compaction block: ascending idx and n
+      uint64_t* wl = reinterpret_cast<uint64_t*>(smem);
+      int* pre = reinterpret_cast<int*>(wl + W);
+      const int n = scan_words(words, W, wl, pre, red);
+      for (int w = threadIdx.x; w < W; w += BLOCK) {
+        uint64_t word = wl[w];
+        int pos = pre[w];
+        while (word) {
+          idx_out[pos++] = w * WAVE + __ffsll((unsigned long long)word) - 1;
+          word &= word - 1;
+        }
       }
+      if (threadIdx.x == 0) {
+        *n_out = n;
+        if (n_log != nullptr) *n_log = n;
+      }
+      return;
     }
-    __syncthreads();
-    if (writer && threadIdx.x == 0) {
-      *n_out = n;
-      if (n_log != nullptr) *n_log = n;
-    }
-  } else {
-    n = min(max(*n_in, 0), ffn);
   }
+  const int g = blockIdx.x % G, s = blockIdx.x / G;
+  const int slot = threadIdx.x / SEG, sl = threadIdx.x % SEG;
+  // the first column this lane touches; Q4 lanes of one block share a block index
+  const int col0 = s * SW + ((WT == W_Q4 && QS == 4) ? (sl >> 2) * 32 : sl * EPC);
+  const bool valid = col0 < d;
+  if constexpr (SCAN) {
+    // the group's words in order (a block-wide pass per 256 words), their counts scanned
+    const int nwg = (W - g + G - 1) / G;
+    int carry = 0;
+    for (int q0 = 0; q0 < nwg; q0 += BLOCK) {
+      const int q = q0 + threadIdx.x;
+      const int w = g + G * q;
+      uint64_t word = (q < nwg) ? words[w] : 0ull;
+      int total;
+      int pos = carry + block_exclusive_scan(__popcll(word), red, &total);
+      while (word) {
+        il[pos++] = w * WAVE + __ffsll((unsigned long long)word) - 1;
+        word &= word - 1;
+      }
+      carry += total;
+    }
+    if (threadIdx.x == 0) s_ng = carry;
+  } else {
+    // the given list, filtered to this group's words, in list order
+    const int n = min(max(*n_in, 0), ffn);
+    const int cap = down_list_cap(W, G);
+    int carry = 0;
+    for (int k0 = 0; k0 < n; k0 += BLOCK) {
+      const int k = k0 + threadIdx.x;
+      const int i = (k < n) ? idx_in[k] : -1;
+      const bool mine = (unsigned)i < (unsigned)ffn && ((i >> 6) & (G - 1)) == g;
+      int total;
+      const int ex = block_exclusive_scan(mine ? 1 : 0, red, &total);
+      if (mine && carry + ex < cap) il[carry + ex] = i;
+      carry += total;
+    }
+    if (threadIdx.x == 0) s_ng = min(carry, cap);
+  }
+  __syncthreads();
+  const int ng = s_ng;
   float acc[NB][EPC];
   float qsum[NB];
 #pragma unroll
@@ -706,23 +967,19 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[t][e] = 0.f;
   }
-  for (int j0 = slot; g + G * j0 < n; j0 += NSL * U) {
+  for (int j0 = slot; j0 < ng; j0 += NSL * U) {
     int ii[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = g + G * (j0 + NSL * u);
-      int i = -1;
-      if (k < n) {
-        if constexpr (SCAN && (XMODE & 2)) {
-          i = idx_in[k];
-        } else if constexpr (SCAN) {
-          const int j = (k - g) / G;
-          i = (j < IDX_LDS) ? il[j] : neuron_at(wl, pre, W, k);
-        }
-        else i = idx_in[k];
-      }
-      ii[u] = ((unsigned)i < (unsigned)ffn) ? i : -1;
+      const int j = j0 + NSL * u;
+      ii[u] = (j < ng) ? il[j] : -1;
     }
+    // activations first (small, likely cached), then the rows
+    float av[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < NB; ++t) av[u][t] = (ii[u] >= 0 && t < B) ? a[(size_t)t * ffn + ii[u]] : 0.f;
     u32x4 w[U];
     float sc[U];
 #pragma unroll
@@ -734,7 +991,8 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
         else if constexpr (WT == W_F32) w[u] = ld_stream(L.w_down_t + ((size_t)ii[u] * d + col0) * 4);
         else {
           const size_t blk = (size_t)ii[u] * (d >> 5) + (col0 >> 5);
-          w[u] = ld_stream(L.w_down_t + blk * 16);
+          if constexpr (QS == 1) w[u] = ld_stream(L.w_down_t + blk * 16);
+          else w[u][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(L.w_down_t + blk * 16) + (sl & 3));
           sc[u] = half_bits_to_float(L.s_down[blk]);
         }
       }
@@ -742,33 +1000,45 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ii[u] < 0) continue;
-      float av[NB];
-#pragma unroll
-      for (int t = 0; t < NB; ++t) av[t] = (t < B) ? a[(size_t)t * ffn + ii[u]] : 0.f;
       if constexpr (WT == W_F16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float lo = h2f_lo(w[u][e]), hi = h2f_hi(w[u][e]);
 #pragma unroll
           for (int t = 0; t < NB; ++t) {
-            acc[t][2 * e] = fmaf(av[t], lo, acc[t][2 * e]);
-            acc[t][2 * e + 1] = fmaf(av[t], hi, acc[t][2 * e + 1]);
+            acc[t][2 * e] = fmaf(av[u][t], lo, acc[t][2 * e]);
+            acc[t][2 * e + 1] = fmaf(av[u][t], hi, acc[t][2 * e + 1]);
           }
         }
       } else if constexpr (WT == W_F32) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int t = 0; t < NB; ++t) acc[t][e] = fmaf(av[t], u2f(w[u][e]), acc[t][e]);
-      } else {
+          for (int t = 0; t < NB; ++t) acc[t][e] = fmaf(av[u][t], u2f(w[u][e]), acc[t][e]);
+      } else if constexpr (QS == 1) {
         float q[32];
         q4_block_codes(w[u], q);
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
-          const float as = av[t] * sc[u];
+          const float as = av[u][t] * sc[u];
           qsum[t] += as;
 #pragma unroll
           for (int e = 0; e < 32; ++e) acc[t][e] = fmaf(q[e], as, acc[t][e]);
+        }
+      } else {
+        const uint32_t cw = w[u][0];
+        float q[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q[e] = (float)((cw >> (8 * e)) & 0xFu);
+          q[4 + e] = (float)((cw >> (8 * e + 4)) & 0xFu);
+        }
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const float as = av[u][t] * sc[u];
+          qsum[t] += as;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(q[e], as, acc[t][e]);
         }
       }
     }
@@ -785,7 +1055,7 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
     if (t >= B) break;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) s_red[slot][sl * EPC + e] = acc[t][e];
+    for (int e = 0; e < EPC; ++e) s_red[slot][down_col<WT, QS>(sl, e)] = acc[t][e];
     __syncthreads();
     for (int c = threadIdx.x; c < SW; c += BLOCK) {
       const int col = s * SW + c;
@@ -819,7 +1089,8 @@ __global__ __launch_bounds__(BLOCK) void k_reduce(const float* __restrict__ part
   if (wave == 0 && i < BD) y[i] = (s4[0][lane] + s4[1][lane]) + (s4[2][lane] + s4[3][lane]);
 }
 
-// Standalone glue: one workgroup per token.
+// Standalone glue: one workgroup per token, d % 4 == 0. Each thread issues all of its
+// 16-byte loads of y (up to GLUE_J) before using them; longer rows take further passes.
 template <bool XF32>
 __global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, const void* __restrict__ x_prev, int d,
                                                 void* __restrict__ x_out) {
@@ -827,13 +1098,39 @@ __global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, con
   __shared__ float red[NWAVES];
   const int t = blockIdx.x;
   const float* yt = y + (size_t)t * d;
+  const int n4 = d >> 2;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += BLOCK) ss = fmaf(yt[c], yt[c], ss);
+  for (int c0 = 0; c0 < n4; c0 += BLOCK * GLUE_J) {
+    u32x4 v[GLUE_J];
+#pragma unroll
+    for (int j = 0; j < GLUE_J; ++j) {
+      const int c = c0 + threadIdx.x + BLOCK * j;
+      v[j] = (c < n4) ? ld16(yt + 4 * c) : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < GLUE_J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(u2f(v[j][e]), u2f(v[j][e]), ss);
+  }
   ss = block_sum(ss, red);
   const float r = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
   const XT* xp = reinterpret_cast<const XT*>(x_prev) + (size_t)t * d;
   XT* xo = reinterpret_cast<XT*>(x_out) + (size_t)t * d;
-  for (int c = threadIdx.x; c < d; c += BLOCK) xo[c] = (r == 0.f) ? xp[c] : (XT)(yt[c] / r);
+  for (int c0 = 0; c0 < n4; c0 += BLOCK * GLUE_J) {
+    u32x4 v[GLUE_J];
+#pragma unroll
+    for (int j = 0; j < GLUE_J; ++j) {
+      const int c = c0 + threadIdx.x + BLOCK * j;
+      v[j] = (c < n4) ? ld16(yt + 4 * c) : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < GLUE_J; ++j) {
+      const int c = c0 + threadIdx.x + BLOCK * j;
+      if (c < n4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[4 * c + e] = (r == 0.f) ? xp[4 * c + e] : (XT)(u2f(v[j][e]) / r);
+    }
+  }
 }
 
 // dst row k = src row perm[k]; row_bytes % 4 == 0 (16-byte vectors when row_bytes % 16 == 0).

@@ -1,6 +1,7 @@
 // Host side of libpi.so: context and scratch, argument checks, kernel selection, stack
 // runner with HIP graphs. See include/pi.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -10,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/pi.h"
+#include "pi.h"
 #include "pi_mfma.hpp"
 
 using namespace pi;
@@ -29,7 +30,7 @@ struct pi_ctx {
   int32_t* idx = nullptr;       // [max_ffn]
   int32_t* nbuf = nullptr;      // [16]
   float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
-  float* part = nullptr;        // [DOWN_G][max_batch][max_d] down-projection partial sums
+  float* part = nullptr;        // [16][max_batch][max_d] down-projection partial sums (groups or K splits)
   float* y = nullptr;           // [max_batch][max_d]
   uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
   uint8_t* xstage = nullptr;    // [max_batch][max_d] fp32-sized
@@ -83,27 +84,38 @@ pi_status fail(pi_ctx* ctx, pi_status s, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Records a hipEvent pair around one kernel launch when the context is profiling.
-struct ProfScope {
-  pi_ctx* c;
-  size_t slot;
-  ProfScope(pi_ctx* ctx, int klass) : c(ctx), slot(SIZE_MAX) {
-    if (!c->profiling) return;
-    if (c->ev_used * 2 + 2 > c->ev.size()) {
-      hipEvent_t a = nullptr, b = nullptr;
-      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
-      c->ev.push_back(a);
-      c->ev.push_back(b);
-      c->ev_class.push_back(klass);
+// The next free pair of profiling events, tagged with a kernel class.
+void prof_slot(pi_ctx* c, int klass, hipEvent_t* e0, hipEvent_t* e1) {
+  if (c->ev_used * 2 + 2 > c->ev.size()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return;
     }
-    slot = c->ev_used++;
-    c->ev_class[slot] = klass;
-    (void)hipEventRecord(c->ev[2 * slot], c->stream);
+    c->ev.push_back(a);
+    c->ev.push_back(b);
+    c->ev_class.push_back(klass);
   }
-  ~ProfScope() {
-    if (slot != SIZE_MAX) (void)hipEventRecord(c->ev[2 * slot + 1], c->stream);
-  }
-};
+  const size_t slot = c->ev_used++;
+  c->ev_class[slot] = klass;
+  *e0 = c->ev[2 * slot];
+  *e1 = c->ev[2 * slot + 1];
+}
+
+// One kernel launch (BLOCK threads per workgroup) on the context's stream. When profiling,
+// the dispatch itself carries a pair of events (hipExtLaunchKernelGGL), so the pair times the
+// kernel's execution, not the queueing around it.
+template <typename... P, typename... A>
+hipError_t launch_k(pi_ctx* c, int klass, void (*kern)(P...), dim3 grid, size_t lds, A... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (c->profiling) prof_slot(c, klass, &e0, &e1);
+  if (e0 != nullptr)
+    hipExtLaunchKernelGGL(kern, grid, dim3(BLOCK), (uint32_t)lds, c->stream, e0, e1, 0u, static_cast<P>(args)...);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(BLOCK), lds, c->stream, static_cast<P>(args)...);
+  return hipGetLastError();
+}
 enum { K_STAGE1 = 0, K_STAGE2, K_TRUEMASK, K_UP, K_DOWN, K_REDUCE, K_COUNT };
 static_assert(K_COUNT == PI_KERNEL_CLASSES, "kernel classes out of sync with pi.h");
 
@@ -140,19 +152,24 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 
 // ---------------------------------------------------------------- kernel dispatch tables
 
+constexpr size_t X_LDS_BUDGET = 65536;  // LDS for staged x that still leaves room for 2 workgroups per CU
+
+// Width of the x column windows for NB tokens of `xe`-byte elements: d when x fits in the LDS
+// budget, else the largest multiple of 512 columns that does. 4 KB of the workgroup's LDS
+// stay free for the kernels' own shared arrays.
+int x_window(const pi_ctx* c, int NB, int d, size_t xe, size_t budget) {
+  const size_t cap = std::min(budget, c->lds_max - 4096);
+  if ((size_t)NB * d * xe <= cap) return d;
+  return std::max(512, (int)(cap / (NB * xe)) / 512 * 512);
+}
+
 template <int NB>
 pi_status launch_stage1_nb(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
-  const size_t budget = 65536;
-  int dc = (int)std::min<size_t>((size_t)L.d, budget / (NB * 2));
-  dc = dc / 512 * 512;
-  if (dc <= 0) dc = L.d;
-  if (dc > L.d) dc = L.d;
+  const int dc = x_window(c, NB, L.d, 2, X_LDS_BUDGET);
   const size_t lds = (size_t)NB * dc * 2;
   PI_HIP(c, allow_lds(k_stage1<NB>, lds));
   const int grid = (L.rank + NWAVES - 1) / NWAVES;
-  ProfScope ps(c, K_STAGE1);
-  hipLaunchKernelGGL(k_stage1<NB>, dim3(grid), dim3(BLOCK), lds, c->stream, L, xin, B, dc, c->z);
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, K_STAGE1, k_stage1<NB>, dim3(grid), lds, L, xin, B, dc, c->z));
   return PI_OK;
 }
 
@@ -171,14 +188,13 @@ constexpr int STAGE2_TILE = 32;  // neurons per workgroup in predictor stage 2
 
 template <int NB, int CPL, bool UP, int WT, int ACT>
 pi_status launch_stage2_t(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
-  const size_t lds = UP ? (size_t)NB * L.d * (WT == W_F32 ? 4 : 2) : 0;
-  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
-  auto kern = k_stage2<NB, CPL, STAGE2_TILE, UP, WT, ACT>;
+  const size_t xe = (WT == W_F32) ? 4 : 2;
+  const int xw = UP ? x_window(c, NB, L.d, xe, c->lds_max) : L.d;
+  const size_t lds = UP ? (size_t)NB * xw * xe : 0;
+  auto kern = k_stage2<NB, CPL, UP, WT, ACT>;
   PI_HIP(c, allow_lds(kern, lds));
-  ProfScope ps(c, K_STAGE2);
-  hipLaunchKernelGGL(kern, dim3(L.ffn / STAGE2_TILE), dim3(BLOCK), lds, c->stream, L, c->z, B, mtok, c->munion,
-                     logits, x, c->a);
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, K_STAGE2, kern, dim3(L.ffn / STAGE2_TILE), lds, L, c->z, B, mtok, c->munion, logits, x, xw,
+                     c->a));
   return PI_OK;
 }
 
@@ -188,12 +204,10 @@ pi_status launch_stage2_c(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, f
   if (L.wtype == W_F16)
     return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_F16, ACT_RELU>(c, L, B, mtok, logits, x)
                              : launch_stage2_t<NB, CPL, true, W_F16, ACT_REGLU>(c, L, B, mtok, logits, x);
-  if constexpr (NB <= 2) {
-    if (L.wtype == W_Q4)
-      return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_Q4, ACT_RELU>(c, L, B, mtok, logits, x)
-                               : launch_stage2_t<NB, CPL, true, W_Q4, ACT_REGLU>(c, L, B, mtok, logits, x);
-  }
-  return fail(c, PI_ERR_UNSUPPORTED, "no predictor path for this weight type and batch");
+  if (L.wtype == W_Q4)
+    return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_Q4, ACT_RELU>(c, L, B, mtok, logits, x)
+                             : launch_stage2_t<NB, CPL, true, W_Q4, ACT_REGLU>(c, L, B, mtok, logits, x);
+  return fail(c, PI_ERR_UNSUPPORTED, "no predictor path for this weight type");
 }
 
 template <int NB>
@@ -215,12 +229,12 @@ template <int WT, int NB, bool UP>
 pi_status launch_truemask_t(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits) {
   constexpr bool XF32 = WT == W_F32;
   const size_t lds = (size_t)NB * L.d * (XF32 ? 4 : 2);
-  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
+  if (lds + 4096 > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
+  if (xin.y != nullptr && (L.d > 4 * BLOCK * GLUE_J || xin.ny > GLUE_NY))
+    return fail(c, PI_ERR_UNSUPPORTED, "chained layers without a predictor need d <= %d", 4 * BLOCK * GLUE_J);
   auto kern = k_truemask<WT, NB, XF32, UP>;
   PI_HIP(c, allow_lds(kern, lds));
-  ProfScope ps(c, K_TRUEMASK);
-  hipLaunchKernelGGL(kern, dim3(L.ffn / 64), dim3(BLOCK), lds, c->stream, L, xin, B, mtok, c->munion, logits, c->a);
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, K_TRUEMASK, kern, dim3(L.ffn / 64), lds, L, xin, B, mtok, c->munion, logits, c->a));
   return PI_OK;
 }
 
@@ -229,10 +243,9 @@ pi_status launch_truemask_w(pi_ctx* c, const LayerDev& L, const XIn& xin, int B,
   switch (nb_for(B)) {
     case 1: return launch_truemask_t<WT, 1, UP>(c, L, xin, B, mtok, logits);
     case 2: return launch_truemask_t<WT, 2, UP>(c, L, xin, B, mtok, logits);
-    case 4: if constexpr (WT != W_Q4) return launch_truemask_t<WT, 4, UP>(c, L, xin, B, mtok, logits); break;
-    default: if constexpr (WT != W_Q4) return launch_truemask_t<WT, 8, UP>(c, L, xin, B, mtok, logits); break;
+    case 4: return launch_truemask_t<WT, 4, UP>(c, L, xin, B, mtok, logits);
+    default: return launch_truemask_t<WT, 8, UP>(c, L, xin, B, mtok, logits);
   }
-  return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
 }
 
 pi_status launch_truemask(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, uint64_t* mtok, float* logits,
@@ -249,15 +262,14 @@ pi_status launch_truemask(pi_ctx* c, const LayerDev& L, const XIn& xin, int B, u
 
 template <int WT, int ACT, int NB>
 pi_status launch_up_t(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
-  const size_t lds = (size_t)NB * L.d * (WT == W_F32 ? 4 : 2);
-  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "batch %d x d %d does not fit in LDS", B, L.d);
+  const size_t xe = (WT == W_F32) ? 4 : 2;
+  const int xw = x_window(c, NB, L.d, xe, c->lds_max);
+  const size_t lds = (size_t)NB * xw * xe;
   auto kern = k_up<WT, ACT, NB>;
   PI_HIP(c, allow_lds(kern, lds));
-  const int per = (ACT == ACT_RELU) ? 2 : 1;
-  const int grid = std::max(1, std::min((L.ffn + NWAVES * per - 1) / (NWAVES * per), 2 * c->cus));
-  ProfScope ps(c, K_UP);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, c->stream, L, x, B, idx_in, n_in, c->a);
-  PI_HIP(c, hipGetLastError());
+  constexpr int CH = NWAVES * ActPW<ACT>::PW;
+  const int grid = std::max(1, std::min((L.ffn + CH - 1) / CH, 8 * c->cus));
+  PI_HIP(c, launch_k(c, K_UP, kern, dim3(grid), lds, L, x, B, xw, idx_in, n_in, c->a));
   return PI_OK;
 }
 
@@ -266,10 +278,9 @@ pi_status launch_up_a(pi_ctx* c, const LayerDev& L, const void* x, int B, const 
   switch (nb_for(B)) {
     case 1: return launch_up_t<WT, ACT, 1>(c, L, x, B, idx_in, n_in);
     case 2: return launch_up_t<WT, ACT, 2>(c, L, x, B, idx_in, n_in);
-    case 4: if constexpr (WT != W_Q4) return launch_up_t<WT, ACT, 4>(c, L, x, B, idx_in, n_in); break;
-    default: if constexpr (WT != W_Q4) return launch_up_t<WT, ACT, 8>(c, L, x, B, idx_in, n_in); break;
+    case 4: return launch_up_t<WT, ACT, 4>(c, L, x, B, idx_in, n_in);
+    default: return launch_up_t<WT, ACT, 8>(c, L, x, B, idx_in, n_in);
   }
-  return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
 }
 
 pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
@@ -287,35 +298,36 @@ pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const in
   }
 }
 
-// Down projection over the active neurons into DOWN_G partial sums (from the union words,
-// SCAN, which also writes idx and n; or from a given index list), then their reduction into y.
-constexpr int DOWN_G = 16;
+// Down projection over the active neurons (from the union words, SCAN, which also writes idx
+// and n; or from a given index list) into DOWN_G partial sums, then (y != nullptr) their sum
+// into y. With y == nullptr the partials stay in c->part for the next layer's glue.
+constexpr int DOWN_G = 8;        // partial sums (groups) at 1..2 tokens
+constexpr int DOWN_G_WIDE = 16;  // at 3..8 tokens, whose union lists are longer
+constexpr int down_groups(int NB) { return NB >= 4 ? DOWN_G_WIDE : DOWN_G; }
 constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
-constexpr int MM_KSD = 16;  // K splits of the batched down projection (<= DOWN_G)
+constexpr int MM_KSD = 16;  // K splits of the batched down projection
 
 template <int WT, int NB, bool SCAN>
 pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
                         int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
-  constexpr int SEG = DownGeom<WT>::SEG;
-  constexpr int U = (WT == W_Q4) ? (NB == 1 ? 4 : 2) : (NB >= 4 ? 4 : 8);
+  constexpr int QS = (WT == W_Q4 && NB > 2) ? 4 : 1;
+  constexpr int U = (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
   const int W = L.ffn / 64;
-  const size_t lds = SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 + (size_t)IDX_LDS * 4 : 0;
-  if (lds > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the index scan", L.ffn);
-  auto kern = k_down_part<WT, NB, SCAN, SEG, U, DOWN_G>;
+  constexpr int G = down_groups(NB);
+  const size_t lds = std::max((size_t)down_list_cap(W, G) * 4, SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
+  constexpr size_t lds_static = (size_t)(BLOCK / DownGeom<WT, QS>::SEG) * (DownGeom<WT, QS>::SW + 1) * 4 + 256;
+  if (lds + lds_static > c->lds_max)
+    return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the down projection", L.ffn);
+  auto kern = k_down_part<WT, NB, SCAN, U, QS, G>;
   PI_HIP(c, allow_lds(kern, lds));
-  const int S = (L.d + DownGeom<WT>::SW - 1) / DownGeom<WT>::SW;
-  {
-    ProfScope ps(c, K_DOWN);
-    hipLaunchKernelGGL(kern, dim3(DOWN_G, S), dim3(BLOCK), lds, c->stream, L, B, c->munion, idx_in, n_in, c->a,
-                       c->part, DOWN_G, idx_out, n_out, n_log);
+  const int S = (L.d + DownGeom<WT, QS>::SW - 1) / DownGeom<WT, QS>::SW;
+  // SCAN: one more block writes idx and n
+  PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a,
+                     c->part, idx_out, n_out, n_log));
+  if (y != nullptr) {
+    const int BD = B * L.d;
+    PI_HIP(c, launch_k(c, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, c->part, G, BD, y));
   }
-  PI_HIP(c, hipGetLastError());
-  const int BD = B * L.d;
-  {
-    ProfScope ps(c, K_REDUCE);
-    hipLaunchKernelGGL(k_reduce, dim3((BD + WAVE - 1) / WAVE), dim3(BLOCK), 0, c->stream, c->part, DOWN_G, BD, y);
-  }
-  PI_HIP(c, hipGetLastError());
   return PI_OK;
 }
 
@@ -325,10 +337,9 @@ pi_status launch_down_w(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   switch (nb_for(B)) {
     case 1: return launch_down_t<WT, 1, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
     case 2: return launch_down_t<WT, 2, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
-    case 4: if constexpr (WT != W_Q4) return launch_down_t<WT, 4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log); break;
-    default: if constexpr (WT != W_Q4) return launch_down_t<WT, 8, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log); break;
+    case 4: return launch_down_t<WT, 4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    default: return launch_down_t<WT, 8, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
   }
-  return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 down projection supports batch <= 2 on this path");
 }
 
 template <bool SCAN>
@@ -362,8 +373,6 @@ pi_status check_batch(pi_ctx* c, const pi_ffn_desc& d, int B) {
       return fail(c, PI_ERR_UNSUPPORTED, "batches above 8 tokens need d and rank multiples of 16");
     return PI_OK;
   }
-  if (d.wtype == PI_W_Q4_0 && B > 2)
-    return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 layers run batches of 1..2 tokens on this path");
   return PI_OK;
 }
 
@@ -387,11 +396,7 @@ pi_status launch_mm_rows(pi_ctx* c, const MmRows& p, dim3 grid, int klass) {
   const size_t lds = (size_t)32 * MT * LDR * 2 * (HILO ? 2 : 1);
   auto kern = k_mm_rows<EPI, ACT, MT, HILO>;
   PI_HIP(c, allow_lds(kern, lds));
-  {
-    ProfScope ps(c, klass);
-    hipLaunchKernelGGL(kern, grid, dim3(BLOCK), lds, c->stream, p);
-  }
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, klass, kern, grid, lds, p));
   return PI_OK;
 }
 
@@ -415,12 +420,8 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
     p.part = c->zpart;
     PI_TRY((launch_mm_rows<EPI_PART, ACT_RELU, MT, false>(c, p, dim3(nt, ks), K_STAGE1)));
     const int BN = B * L.rank;
-    {
-      ProfScope ps(c, K_REDUCE);
-      hipLaunchKernelGGL(k_reduce_hilo, dim3((BN + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, c->stream, c->zpart, ks, BN,
-                         c->zhi, c->zlo);
-    }
-    PI_HIP(c, hipGetLastError());
+    PI_HIP(c, launch_k(c, K_REDUCE, k_reduce_hilo, dim3((BN + BLOCK - 1) / BLOCK), 0, c->zpart, ks, BN, c->zhi,
+                       c->zlo));
     // stage 2: v = Z W2^T + b_p with the mask epilogue
     MmRows q{};
     q.x = c->zhi;
@@ -485,28 +486,15 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   q.ks_len = ((L.ffn + MM_KSD - 1) / MM_KSD + 15) / 16 * 16;
   const int ks = (L.ffn + q.ks_len - 1) / q.ks_len;
   q.part = c->part;
-  {
-    ProfScope ps(c, K_DOWN);
-    hipLaunchKernelGGL(k_mm_down<MT>, dim3((L.d + 511) / 512, ks), dim3(BLOCK), 0, c->stream, q);
-  }
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, K_DOWN, k_mm_down<MT>, dim3((L.d + 511) / 512, ks), 0, q));
   const int BD = B * L.d;
-  {
-    ProfScope ps(c, K_REDUCE);
-    hipLaunchKernelGGL(k_reduce, dim3((BD + WAVE - 1) / WAVE), dim3(BLOCK), 0, c->stream, c->part, ks, BD, y);
-  }
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, c->part, ks, BD, y));
   return PI_OK;
 }
 
 pi_status launch_compact_log(pi_ctx* c, int ffn, int32_t* idx, int32_t* n, int32_t* n_log) {
   const int W = ffn / 64;
-  {
-    ProfScope ps(c, K_REDUCE);
-    hipLaunchKernelGGL(k_compact, dim3((W + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, c->stream, c->munion, W, idx, n,
-                       n_log);
-  }
-  PI_HIP(c, hipGetLastError());
+  PI_HIP(c, launch_k(c, K_REDUCE, k_compact, dim3((W + BLOCK - 1) / BLOCK), 0, c->munion, W, idx, n, n_log));
   return PI_OK;
 }
 
@@ -598,7 +586,7 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   const size_t o_idx = off; off += al(F * 4);
   const size_t o_n = off; off += al(16 * 4);
   const size_t o_a = off; off += al(B * F * 4);
-  const size_t o_part = off; off += al((size_t)DOWN_G * B * D * 4);
+  const size_t o_part = off; off += al((size_t)std::max(DOWN_G_WIDE, MM_KSD) * B * D * 4);
   const size_t o_y = off; off += al(B * D * 4);
   const size_t o_x0 = off; off += al(B * D * 4);
   const size_t o_x1 = off; off += al(B * D * 4);
@@ -728,7 +716,7 @@ pi_status pi_predict(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, u
     PI_TRY(batched_predict(ctx, L, x, B, mask, logits_out));
     return launch_compact(ctx, L.ffn, idx, n_active);
   }
-  const XIn xin{x, nullptr, nullptr};
+  const XIn xin{x, nullptr, nullptr, 1, 0};
   if (L.rank > 0) {
     PI_TRY(launch_stage1(ctx, L, xin, B));
     PI_TRY(launch_stage2(ctx, L, B, mask, logits_out, nullptr));
@@ -767,7 +755,7 @@ pi_status pi_layer(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, flo
   PI_HIP(ctx, hipSetDevice(ctx->device));
   if (B > 8)
     return enqueue_batched(ctx, ffn, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
-  const XIn xin{x, nullptr, nullptr};
+  const XIn xin{x, nullptr, nullptr, 1, 0};
   return enqueue_layer(ctx, ffn, xin, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
 }
 
@@ -876,14 +864,29 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
       XIn xin;
       const void* x_cur;
       if (l == 0) {
-        xin = XIn{ctx->xstage, nullptr, nullptr};
+        xin = XIn{ctx->xstage, nullptr, nullptr, 1, 0};
         x_cur = ctx->xstage;
+      } else if (B > 1) {
+        // several tokens: every predictor workgroup would re-read B x d partial sums, so the
+        // partials are added and the glue applied once, by two small kernels
+        const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
+        const int BD = B * d;
+        PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part,
+                             down_groups(nb_for(B)), BD, ctx->y));
+        if (xe == 4)
+          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<true>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
+        else
+          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
+        xin = XIn{ctx->xbuf[l & 1], nullptr, nullptr, 1, 0};
+        x_cur = ctx->xbuf[l & 1];
       } else {
         const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-        xin = XIn{x_prev, ctx->y, ctx->xbuf[l & 1]};
+        // the glue adds the previous layer's partial sums itself
+        xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], DOWN_G, B * d};
         x_cur = ctx->xbuf[l & 1];
       }
-      PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, ctx->y, nullptr, ctx->idx, ctx->nbuf, ctx->nlog + l));
+      PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, l == L - 1 ? ctx->y : nullptr, nullptr, ctx->idx,
+                           ctx->nbuf, ctx->nlog + l));
     }
     return PI_OK;
   };

@@ -19,7 +19,10 @@
  *    failures return PI_ERR_HIP. pi_last_error(ctx) gives a human-readable reason.
  *  - Compute entry points allocate nothing: every scratch buffer (activations, partial
  *    sums, mask words, staging) belongs to the pi_ctx and is sized at pi_ctx_create.
- *  - No C++ exception crosses this boundary. A pi_ctx is used by one host thread at a time.
+ *  - No C++ exception crosses this boundary. A pi_ctx is used by one host thread at a time,
+ *    and the work of one context must not run concurrently with itself (its scratch, and
+ *    the arrival counts its down projection keeps at zero between calls, are shared): keep
+ *    a context's calls on one stream, or order them.
  *  - Neuron index space: the "stored" order of the layer's rows. With a hot-first layout
  *    (pi_permute_rows), neuron_table[k] maps stored row k back to its original neuron.
  */
@@ -113,7 +116,7 @@ void pi_ffn_destroy(pi_ffn *ffn);
  *             list when B == 1); entries at and beyond n_active are unspecified
  *   n_active  device int32 scalar: length of idx
  *   logits_out nullable fp32 [B][ffn]: the decision values themselves (for checking)
- *   B         1..max_batch (at most 64); 1..8 run on the vector units (Q4_0: 1..2), 9..64 on the
+ *   B         1..max_batch (at most 64); 1..8 run on the vector units, 9..64 on the
  *             matrix cores (fp16 weights, d and rank multiples of 16); mask words are then
  *             written as 32-bit halves (same bit layout) */
 pi_status pi_predict(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, uint64_t *mask,
@@ -157,15 +160,17 @@ pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, cons
 /* Kernel classes of pi_stack_profile's outputs, in this order:
  * predictor stage 1 (with the glue); predictor stage 2 + threshold + the activations of the
  * workgroup's own active neurons; true-mask threshold GEMV + activations; gathered up/gate
- * GEMV of the index-list entry point; down projection into partial sums (with the index
- * scan); reduction of the partial sums into y. */
+ * GEMV of the index-list entry point; down projection (with the index scan) into partial
+ * sums that the last workgroup of each column slice adds into y; the separate reduction
+ * kernels of the matrix-core path (partial sums, compaction, predictor hi/lo split). */
 #define PI_KERNEL_CLASSES 6
 
-/* pi_stack_run without a graph, with a hipEvent pair recorded on the context's stream around
- * every kernel launch. Blocks until the work is done, then writes the summed event time in
+/* pi_stack_run without a graph, every kernel dispatched with a pair of hipEvents
+ * (hipExtLaunchKernelGGL) on the context's stream, so each pair times that kernel's own
+ * execution. Blocks until the work is done, then writes the summed event time in
  * milliseconds (ms_out[PI_KERNEL_CLASSES], host) and the number of launches
  * (launches_out[PI_KERNEL_CLASSES], host) of each kernel class. Other arguments as for
- * pi_stack_run. For measurement; the events add a little dispatch time to every launch. */
+ * pi_stack_run. For measurement. */
 pi_status pi_stack_profile(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, const void *x_tokens,
                            int32_t T, int32_t B, float *y_out, int32_t *n_active_log, double *ms_out,
                            int64_t *launches_out);

@@ -92,6 +92,15 @@ CASES = {
     "f16-b8": (_cfg("opt6.7b", d=2048, ffn=8192, rank=1024), 1, 16, 8),
     "reglu-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 1, 8, 8),
     "f32-b3": (_cfg("tiny"), 0, 9, 3),
+    # Q4_0 batches of 3..8 (quarter-block down lanes), ReGLU on Q4_0, x in column windows
+    "q4-b4": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 1, 8, 4),
+    "q4-b8": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 2, 16, 8),
+    "q4-b5-ragged": (_cfg("opt175b", d=544, ffn=320, rank=136), 0, 10, 5),
+    "q4-reglu-b8": (_cfg("opt175b", act="reglu", d=1024, ffn=2048, rank=512), 0, 8, 8),
+    "q4-truemask-b8": (_cfg("opt175b", d=544, ffn=320, rank=None), 0, 8, 8),
+    "reglu-truemask-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 0, 8, 8),
+    "f16-b8-xwindows": (_cfg("opt6.7b", d=12288, ffn=2048, rank=512), 0, 8, 8),
+    "opt175-full-q4-b8": (_cfg("opt175b"), 0, 8, 8),
     # batched path on the matrix cores (9..64 tokens)
     "relu-b16-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 32, 16),
     "reglu-b64-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 2, 64, 64),
@@ -154,6 +163,27 @@ def test_predict_then_sparse_ffn_equals_layer_bitwise():
         assert torch.equal(y, out["y"])
         out2 = run_layer(ctx, ffn, xb)
         assert torch.equal(out2["y"], out["y"]), "layer is not deterministic"
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_predict_then_sparse_ffn_equals_layer_bitwise_q4(B):
+    """Same identity on Q4_0 weights, with x in column windows at 8 tokens (d = 12288)."""
+    cfg = _cfg("opt175b", ffn=2048, rank=512)
+    L = make_layer(cfg, 1, device="cuda")
+    x = make_tokens(cfg, B, device="cuda")
+    ctx = make_ctx([L])
+    ffn = pi.Ffn(ctx, L)
+    out = run_layer(ctx, ffn, x)
+    mask = torch.zeros_like(out["mask"])
+    idx = torch.full_like(out["idx"], -1)
+    n = torch.full_like(out["n"], -1)
+    pi.predict(ctx, ffn, x, mask, idx, n)
+    y = torch.empty_like(out["y"])
+    pi.sparse_ffn(ctx, ffn, x, idx, n, y)
+    torch.cuda.synchronize()
+    assert torch.equal(mask, out["mask"]) and int(n.item()) == int(out["n"].item())
+    assert torch.equal(y, out["y"])
+    check_layer(L.to_host(), x.cpu().numpy(), out, TOL["q4_0"])
 
 
 def test_sparse_ffn_on_oracle_index_list():
@@ -301,7 +331,7 @@ def test_invalid_arguments_enqueue_nothing():
     Lq = make_layer(q4, 0, device="cuda")
     fq = pi.Ffn(big, Lq)
     with pytest.raises(pi.PiError, match="unsupported"):
-        pi.layer(big, fq, x70[:4].contiguous(), y70[:4])  # Q4_0 above 2 tokens
+        pi.layer(big, fq, x70[:12].contiguous(), y70[:12])  # Q4_0 above 8 tokens
 
 
 def test_stack_batched_graph_equals_eager():
