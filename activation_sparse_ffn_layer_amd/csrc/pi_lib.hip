@@ -30,7 +30,7 @@ struct pi_ctx {
   int32_t* idx = nullptr;       // [max_ffn]
   int32_t* nbuf = nullptr;      // [16]
   float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
-  float* part = nullptr;        // [16][max_batch][max_d] down-projection partial sums (groups or K splits)
+  float* part = nullptr;        // [32][max_batch][max_d] down-projection partial sums (groups or K splits)
   float* y = nullptr;           // [max_batch][max_d]
   uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
   uint8_t* xstage = nullptr;    // [max_batch][max_d] fp32-sized
@@ -39,7 +39,7 @@ struct pi_ctx {
   float* zpart = nullptr;       // [MM_KS1][max_batch][max_rank]
   half_t* zhi = nullptr;        // [max_batch][max_rank]
   half_t* zlo = nullptr;
-  half_t* a16 = nullptr;        // [32 * MT][lda] activations at compacted positions
+  half_t* a16 = nullptr;        // [32 or 64][lda] activations at compacted positions
   int lda = 0;
   std::string err;
   // cached graph of one stack step, captured on a private stream (the caller's stream may be
@@ -305,7 +305,7 @@ constexpr int DOWN_G = 8;        // partial sums (groups) at 1..2 tokens
 constexpr int DOWN_G_WIDE = 16;  // at 3..8 tokens, whose union lists are longer
 constexpr int down_groups(int NB) { return NB >= 4 ? DOWN_G_WIDE : DOWN_G; }
 constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
-constexpr int MM_KSD = 16;  // K splits of the batched down projection
+constexpr int MM_KSD = 32;  // K splits of the batched down projection
 
 template <int WT, int NB, bool SCAN>
 pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
@@ -390,17 +390,17 @@ pi_status check_dev_ptr(pi_ctx* c, const void* p, const char* name, bool nullabl
 
 // ---------------------------------------------------------------- batched path (9..64 tokens)
 
-template <int EPI, int ACT, int MT, bool HILO>
-pi_status launch_mm_rows(pi_ctx* c, const MmRows& p, dim3 grid, int klass) {
-  constexpr int LDR = MM_KW + 8;
-  const size_t lds = (size_t)32 * MT * LDR * 2 * (HILO ? 2 : 1);
-  auto kern = k_mm_rows<EPI, ACT, MT, HILO>;
+// One tiled product (k_mm_gemm) over `ncols` output columns and ks K splits.
+template <int EPI, int ACT, bool HILO>
+pi_status launch_mm(pi_ctx* c, const MmRows& p, int ncols, int ks, int klass) {
+  constexpr int NPW = (EPI == EPI_ACT && ACT == ACT_REGLU) ? 32 : 64;
+  const size_t lds = mm_gemm_lds<HILO>();
+  auto kern = k_mm_gemm<EPI, ACT, HILO>;
   PI_HIP(c, allow_lds(kern, lds));
-  PI_HIP(c, launch_k(c, klass, kern, grid, lds, p));
+  PI_HIP(c, launch_k(c, klass, kern, dim3((ncols + NPW - 1) / NPW, ks), lds, p));
   return PI_OK;
 }
 
-template <int MT>
 pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint32_t* mtok, float* logits) {
   MmRows p{};
   p.B = B;
@@ -413,12 +413,12 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
     p.ldx = L.d;
     p.w0 = reinterpret_cast<const half_t*>(L.p_w1);
     p.N = L.rank;
-    const int nt = (L.rank + 127) / 128;
-    int ks = std::max(1, std::min(MM_KS1, 256 / nt));
-    p.ks_len = ((L.d + ks - 1) / ks + MM_KW - 1) / MM_KW * MM_KW;
+    const int nt = (L.rank + 63) / 64;
+    int ks = std::max(1, std::min(MM_KS1, 512 / nt));
+    p.ks_len = ((L.d + ks - 1) / ks + MG_KC - 1) / MG_KC * MG_KC;
     ks = (L.d + p.ks_len - 1) / p.ks_len;
     p.part = c->zpart;
-    PI_TRY((launch_mm_rows<EPI_PART, ACT_RELU, MT, false>(c, p, dim3(nt, ks), K_STAGE1)));
+    PI_TRY((launch_mm<EPI_PART, ACT_RELU, false>(c, p, L.rank, ks, K_STAGE1)));
     const int BN = B * L.rank;
     PI_HIP(c, launch_k(c, K_REDUCE, k_reduce_hilo, dim3((BN + BLOCK - 1) / BLOCK), 0, c->zpart, ks, BN, c->zhi,
                        c->zlo));
@@ -438,7 +438,7 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
     q.mask_union = reinterpret_cast<uint32_t*>(c->munion);
     q.logits = logits;
     q.ffn = L.ffn;
-    return launch_mm_rows<EPI_MASK, ACT_RELU, MT, true>(c, q, dim3((L.ffn + 127) / 128, 1), K_STAGE2);
+    return launch_mm<EPI_MASK, ACT_RELU, true>(c, q, L.ffn, 1, K_STAGE2);
   }
   // no predictor: the true pre-activation of the masked projection
   p.x = x;
@@ -451,10 +451,9 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
   p.mask_tok = mtok;
   p.mask_union = reinterpret_cast<uint32_t*>(c->munion);
   p.logits = logits;
-  return launch_mm_rows<EPI_MASK, ACT_RELU, MT, false>(c, p, dim3((L.ffn + 127) / 128, 1), K_TRUEMASK);
+  return launch_mm<EPI_MASK, ACT_RELU, false>(c, p, L.ffn, 1, K_TRUEMASK);
 }
 
-template <int MT>
 pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int32_t* idx, const int32_t* n,
                  float* y) {
   MmRows p{};
@@ -471,9 +470,8 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   p.a16 = c->a16;
   p.lda = c->lda;
   p.ffn = L.ffn;
-  const dim3 grid((L.ffn + 127) / 128, 1);
-  if (L.act == ACT_RELU) PI_TRY((launch_mm_rows<EPI_ACT, ACT_RELU, MT, false>(c, p, grid, K_UP)));
-  else PI_TRY((launch_mm_rows<EPI_ACT, ACT_REGLU, MT, false>(c, p, grid, K_UP)));
+  if (L.act == ACT_RELU) PI_TRY((launch_mm<EPI_ACT, ACT_RELU, false>(c, p, L.ffn, 1, K_UP)));
+  else PI_TRY((launch_mm<EPI_ACT, ACT_REGLU, false>(c, p, L.ffn, 1, K_UP)));
   MmDown q{};
   q.a16 = c->a16;
   q.lda = c->lda;
@@ -483,10 +481,14 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   q.n_dev = n;
   q.ffn = L.ffn;
   q.d = L.d;
-  q.ks_len = ((L.ffn + MM_KSD - 1) / MM_KSD + 15) / 16 * 16;
-  const int ks = (L.ffn + q.ks_len - 1) / q.ks_len;
+  // K splits: enough workgroups to fill the chip, each split at most MD_SPLIT_MAX positions
+  const int cblocks = (L.d + 511) / 512;
+  int ks = std::min(MM_KSD, std::max((512 + cblocks - 1) / cblocks, (L.ffn + MD_SPLIT_MAX - 1) / MD_SPLIT_MAX));
+  q.ks_len = ((L.ffn + ks - 1) / ks + 15) / 16 * 16;
+  if (q.ks_len > MD_SPLIT_MAX) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the batched path", L.ffn);
+  ks = (L.ffn + q.ks_len - 1) / q.ks_len;
   q.part = c->part;
-  PI_HIP(c, launch_k(c, K_DOWN, k_mm_down<MT>, dim3((L.d + 511) / 512, ks), 0, q));
+  PI_HIP(c, launch_k(c, K_DOWN, k_mm_down, dim3(cblocks, ks), 0, q));
   const int BD = B * L.d;
   PI_HIP(c, launch_k(c, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, c->part, ks, BD, y));
   return PI_OK;
@@ -501,13 +503,13 @@ pi_status launch_compact_log(pi_ctx* c, int ffn, int32_t* idx, int32_t* n, int32
 pi_status batched_predict(pi_ctx* c, const LayerDev& L, const void* x, int B, uint64_t* mask, float* logits) {
   uint32_t* mt = reinterpret_cast<uint32_t*>(mask);
   const half_t* xh = static_cast<const half_t*>(x);
-  return B <= 32 ? mm_predict<1>(c, L, xh, B, mt, logits) : mm_predict<2>(c, L, xh, B, mt, logits);
+  return mm_predict(c, L, xh, B, mt, logits);
 }
 
 pi_status batched_ffn(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx, const int32_t* n,
                       float* y) {
   const half_t* xh = static_cast<const half_t*>(x);
-  return B <= 32 ? mm_ffn<1>(c, L, xh, B, idx, n, y) : mm_ffn<2>(c, L, xh, B, idx, n, y);
+  return mm_ffn(c, L, xh, B, idx, n, y);
 }
 
 pi_status enqueue_batched(pi_ctx* c, const pi_ffn* f, const void* x, int B, float* y, uint64_t* mask, int32_t* idx,

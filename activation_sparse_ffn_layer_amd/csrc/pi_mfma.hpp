@@ -28,7 +28,7 @@ enum { EPI_PART = 0, EPI_MASK = 1, EPI_ACT = 2 };
 
 // Arguments of the row-tiled product C[t][n] = sum_k X[t][k] W[row(n)][k].
 struct MmRows {
-  const half_t* x;       // [Bp][K] fp16 (Bp = 32*MT rows, rows >= B ignored)
+  const half_t* x;       // [B][ldx] fp16 token rows
   const half_t* x_lo;    // HILO: low halves of X
   int B, K, ldx;
   const half_t* w0;      // rows of K halves: W1, W2, or up (ReLU) / gate (ReGLU)
@@ -49,124 +49,157 @@ struct MmRows {
   int ffn;
 };
 
-constexpr int MM_KW = 256;  // K window staged in LDS per step of the workgroup
+// ---------------------------------------------------------------------------------------
+// k_mm_gemm: the row-tiled products C[t][n] = sum_k X[t][k] W[row(n)][k], tiled through LDS. A workgroup owns 64
+// weight rows (ReGLU activations: 32 neurons' gate rows then their up rows) and all 64 token
+// rows of X, and walks K in chunks of MG_KC halves. Every thread loads 16-byte pieces of 4
+// weight rows and 4 X rows per chunk (16 lanes cover a row's 256-byte piece: coalesced), the
+// next chunk's pieces are loaded while the current chunk, staged in LDS, feeds the MFMAs.
+// Wave w computes the 32 x 32 block (tokens 32*(w>>1).., rows 32*(w&1)..).
+// K (and every K split) is a multiple of 16; tokens >= B and rows past N are zeros.
+// ---------------------------------------------------------------------------------------
+constexpr int MG_KC = 128;         // K chunk (halves)
+constexpr int MG_P = MG_KC + 8;    // LDS row pitch (halves): 16-byte skew between rows
 
-template <int EPI, int ACT, int MT, bool HILO>
-__global__ __launch_bounds__(BLOCK) void k_mm_rows(MmRows p) {
-  constexpr int LDR = MM_KW + 8;  // padded LDS row (halves): 16-byte skew between rows
+template <bool HILO>
+constexpr size_t mm_gemm_lds() { return (size_t)(HILO ? 3 : 2) * 64 * MG_P * 2; }
+
+template <int EPI, int ACT, bool HILO>
+__global__ __launch_bounds__(BLOCK) void k_mm_gemm(MmRows p) {
+  constexpr bool GU = (EPI == EPI_ACT && ACT == ACT_REGLU);  // rows = gate rows, then up rows
+  constexpr int NPW = GU ? 32 : 64;                          // output columns per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  half_t* xs = reinterpret_cast<half_t*>(smem);         // [32*MT][LDR]
-  half_t* xl = xs + 32 * MT * LDR;                      // HILO: low halves
+  half_t* ws = reinterpret_cast<half_t*>(smem);  // [64][MG_P] weight rows
+  half_t* xs = ws + 64 * MG_P;                   // [64][MG_P] X rows
+  half_t* xls = xs + 64 * MG_P;                  // HILO: low halves of X
+  __shared__ uint32_t s_union[2];
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int N = (p.n_dev != nullptr) ? min(*p.n_dev, p.ffn) : p.N;
-  const int n0 = (blockIdx.x * NWAVES + wave) * 32;
-  if (blockIdx.x * NWAVES * 32 >= N) return;  // whole workgroup past the end (uniform)
-  const int n = n0 + (lane & 31);
-  const bool valid = n < N;
-  int row = valid ? ((p.idx != nullptr) ? p.idx[n] : n) : 0;
-  if ((unsigned)row >= (unsigned)(p.idx != nullptr ? p.ffn : N)) row = 0;
-  const int kh = 8 * (lane >> 5);
+  const int N = (p.n_dev != nullptr) ? min(max(*p.n_dev, 0), p.ffn) : p.N;
+  const int nb = blockIdx.x * NPW;
+  if (nb >= N) return;  // uniform over the workgroup
+  // load slots: tile rows rr = tid/16 + 16j (j < 4), piece tid%16 of the chunk
+  const int piece = threadIdx.x & 15;
+  const half_t* wp[4];
+  const half_t* xp[4];
+  const half_t* xlp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rr = (threadIdx.x >> 4) + 16 * j;
+    const int col = nb + (GU ? (rr & 31) : rr);
+    wp[j] = nullptr;
+    if (col < N) {
+      int row = (p.idx != nullptr) ? p.idx[col] : col;
+      if ((unsigned)row >= (unsigned)(p.idx != nullptr ? p.ffn : N)) row = 0;
+      const half_t* base = (GU && rr >= 32) ? p.w1 : p.w0;
+      wp[j] = base + (size_t)row * p.K + piece * 8;
+    }
+    xp[j] = (rr < p.B) ? p.x + (size_t)rr * p.ldx + piece * 8 : nullptr;
+    xlp[j] = (HILO && rr < p.B) ? p.x_lo + (size_t)rr * p.ldx + piece * 8 : nullptr;
+  }
   const int k_begin = blockIdx.y * p.ks_len, k_end = min(p.K, k_begin + p.ks_len);
-  const half_t* r0 = p.w0 + (size_t)row * p.K + kh;
-  const half_t* r1 = (ACT == ACT_REGLU && EPI == EPI_ACT) ? p.w1 + (size_t)row * p.K + kh : nullptr;
-  f16v acc0[MT], acc1[MT];
+  u32x4 wr[4], xr[4], xlr[4];
+  auto load = [&](int kc) {
+    const int off = kc + piece * 8;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    acc0[m] = (f16v){};
-    acc1[m] = (f16v){};
-  }
-  const int rows_x = 32 * MT;
-  for (int w0 = k_begin; w0 < k_end; w0 += MM_KW) {
-    const int kw = min(MM_KW, k_end - w0);
-    __syncthreads();
-    // stage X[:, w0 : w0+kw] (16-byte pieces); rows >= B are zeros
-    for (int q = threadIdx.x; q < rows_x * (MM_KW / 8); q += BLOCK) {
-      const int t = q / (MM_KW / 8), c = (q % (MM_KW / 8)) * 8;
-      u32x4 v = (u32x4){0, 0, 0, 0}, vl = (u32x4){0, 0, 0, 0};
-      if (t < p.B && c < kw) {
-        v = ld16(p.x + (size_t)t * p.ldx + w0 + c);
-        if constexpr (HILO) vl = ld16(p.x_lo + (size_t)t * p.ldx + w0 + c);
-      }
-      *reinterpret_cast<u32x4*>(xs + t * LDR + c) = v;
-      if constexpr (HILO) *reinterpret_cast<u32x4*>(xl + t * LDR + c) = vl;
+    for (int j = 0; j < 4; ++j) {
+      const bool in = off < k_end;
+      wr[j] = (in && wp[j] != nullptr) ? ld_stream(wp[j] + kc) : (u32x4){0, 0, 0, 0};
+      xr[j] = (in && xp[j] != nullptr) ? ld16(xp[j] + kc) : (u32x4){0, 0, 0, 0};
+      if constexpr (HILO) xlr[j] = (in && xlp[j] != nullptr) ? ld16(xlp[j] + kc) : (u32x4){0, 0, 0, 0};
+    }
+  };
+  f16v acc = (f16v){};
+  const int rb = wave & 1, tb = wave >> 1;
+  const int kh = 8 * (lane >> 5);
+  const half_t* wrd = ws + (32 * rb + (lane & 31)) * MG_P + kh;
+  const half_t* xrd = xs + (32 * tb + (lane & 31)) * MG_P + kh;
+  const half_t* xlrd = xls + (32 * tb + (lane & 31)) * MG_P + kh;
+  if (k_begin < k_end) load(k_begin);
+  for (int kc = k_begin; kc < k_end; kc += MG_KC) {
+    __syncthreads();  // the previous chunk's reads of LDS are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = (threadIdx.x >> 4) + 16 * j;
+      *reinterpret_cast<u32x4*>(ws + rr * MG_P + piece * 8) = wr[j];
+      *reinterpret_cast<u32x4*>(xs + rr * MG_P + piece * 8) = xr[j];
+      if constexpr (HILO) *reinterpret_cast<u32x4*>(xls + rr * MG_P + piece * 8) = xlr[j];
     }
     __syncthreads();
-    constexpr int U = 4;
-    for (int k = 0; k < kw; k += 16 * U) {
-      u32x4 b0[U], b1[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool in = valid && (k + 16 * u < kw);
-        b0[u] = in ? ld_stream(r0 + w0 + k + 16 * u) : (u32x4){0, 0, 0, 0};
-        if constexpr (ACT == ACT_REGLU && EPI == EPI_ACT) b1[u] = in ? ld_stream(r1 + w0 + k + 16 * u) : (u32x4){0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k + 16 * u >= kw) break;
-        const h8 bb0 = __builtin_bit_cast(h8, b0[u]);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const int xr = (32 * m + (lane & 31)) * LDR + k + 16 * u + kh;
-          const h8 a = __builtin_bit_cast(h8, ld16(xs + xr));
-          acc0[m] = mfma(a, bb0, acc0[m]);
-          if constexpr (HILO) acc0[m] = mfma(__builtin_bit_cast(h8, ld16(xl + xr)), bb0, acc0[m]);
-          if constexpr (ACT == ACT_REGLU && EPI == EPI_ACT) acc1[m] = mfma(a, __builtin_bit_cast(h8, b1[u]), acc1[m]);
-        }
-      }
+    if (kc + MG_KC < k_end) load(kc + MG_KC);  // next chunk in flight during the MFMAs
+    const int kw = min(MG_KC, k_end - kc);
+    for (int k = 0; k < kw; k += 16) {
+      const h8 b = __builtin_bit_cast(h8, ld16(wrd + k));
+      acc = mfma(__builtin_bit_cast(h8, ld16(xrd + k)), b, acc);
+      if constexpr (HILO) acc = mfma(__builtin_bit_cast(h8, ld16(xlrd + k)), b, acc);
     }
   }
-  // ---- epilogues
+  // ---- epilogues: acc[r] = C[token 32 tb + mfma_row(r, lane)][tile row 32 rb + lane % 32]
+  const int col = nb + (GU ? (lane & 31) : 32 * rb + (lane & 31));
+  const bool valid = col < N;
   if constexpr (EPI == EPI_PART) {
     if (valid) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * m + mfma_row(r, lane);
-          if (t < p.B) p.part[((size_t)blockIdx.y * p.B + t) * N + n] = acc0[m][r];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * tb + mfma_row(r, lane);
+        if (t < p.B) p.part[((size_t)blockIdx.y * p.B + t) * N + col] = acc[r];
+      }
     }
   } else if constexpr (EPI == EPI_MASK) {
-    const float bias = valid ? p.bias[n] : 0.f;
+    const float bias = valid ? p.bias[col] : 0.f;
     const int W32 = p.ffn >> 5;
     bool any = false;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * m + mfma_row(r, lane);
-        const float v = acc0[m][r] + bias;
-        const bool bit = valid && t < p.B && v > p.threshold;
-        any |= bit;
-        const uint64_t bal = __ballot(bit);
-        if (p.mask_tok != nullptr && (lane & 31) == 0 && t < p.B)
-          p.mask_tok[(size_t)t * W32 + (n0 >> 5)] = (uint32_t)(bal >> (lane & 32));
-        if (p.logits != nullptr && valid && t < p.B) p.logits[(size_t)t * p.N + n] = v;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * tb + mfma_row(r, lane);
+      const float v = acc[r] + bias;
+      const bool bit = valid && t < p.B && v > p.threshold;
+      any |= bit;
+      const uint64_t bal = __ballot(bit);
+      if (p.mask_tok != nullptr && (lane & 31) == 0 && t < p.B)
+        p.mask_tok[(size_t)t * W32 + ((nb + 32 * rb) >> 5)] = (uint32_t)(bal >> (lane & 32));
+      if (p.logits != nullptr && valid && t < p.B) p.logits[(size_t)t * p.N + col] = v;
+    }
     const uint64_t u = __ballot(any);
-    if (lane == 0) p.mask_union[n0 >> 5] = (uint32_t)u | (uint32_t)(u >> 32);
-  } else {  // EPI_ACT: a16[t][n] for compacted position n
-    const float bias = valid ? p.bias[row] : 0.f;
+    const uint32_t u32 = (uint32_t)u | (uint32_t)(u >> 32);
+    // the two token halves of a row block: OR through LDS
+    if (tb == 1 && lane == 0) s_union[rb] = u32;
+    __syncthreads();
+    if (tb == 0 && lane == 0) p.mask_union[(nb + 32 * rb) >> 5] = u32 | s_union[rb];
+  } else {  // EPI_ACT: a16[t][col] at compacted position col
+    const int npad = (N + 15) & ~15;
+    if constexpr (GU) {
+      // up accumulators (rb = 1) meet the gate ones (rb = 0) through LDS (the tiles are free now)
+      __syncthreads();
+      float* ex = reinterpret_cast<float*>(smem);  // [2 tb][16 r][64 lanes]
+      if (rb == 1) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+        for (int r = 0; r < 16; ++r) ex[(tb * 16 + r) * WAVE + lane] = acc[r];
+      }
+      __syncthreads();
+      if (rb == 0 && col < npad) {
+        const float bias = valid ? p.bias[p.idx != nullptr ? p.idx[col] : col] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * tb + mfma_row(r, lane);
+          const float up = ex[(tb * 16 + r) * WAVE + lane];
+          const float a = (valid && t < p.B) ? fmaxf(acc[r] + bias, 0.f) * up : 0.f;
+          if (t < p.B) p.a16[(size_t)t * p.lda + col] = (half_t)a;
+        }
+      }
+    } else if (col < npad) {
+      const float bias = valid ? p.bias[p.idx != nullptr ? p.idx[col] : col] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 32 * m + mfma_row(r, lane);
-        float a = 0.f;
-        if (valid && t < p.B) {
-          if constexpr (ACT == ACT_RELU) a = fmaxf(acc0[m][r] + bias, 0.f);
-          else a = fmaxf(acc0[m][r] + bias, 0.f) * acc1[m][r];
-        }
-        if (n < ((N + 15) & ~15)) p.a16[(size_t)t * p.lda + n] = (half_t)a;
+        const int t = 32 * tb + mfma_row(r, lane);
+        const float a = (valid && t < p.B) ? fmaxf(acc[r] + bias, 0.f) : 0.f;
+        if (t < p.B) p.a16[(size_t)t * p.lda + col] = (half_t)a;
       }
+    }
   }
 }
 
-// Down projection y_part[ks][t][c] = sum over positions k of split ks of a16[t][k] *
-// w_down_t[idx[k]][c]. A wave owns 128 columns (4 per lane of a half-wave: one 8-byte load
-// per row) and walks its K split 16 positions at a time: lanes of half h load rows
-// k + 8h .. k + 8h + 7, so each lane holds the 8 K values of its 4 columns and feeds four
-// MFMAs whose output columns are {4*(l%32) + j}.
+// Arguments of the batched down projection part[ks][t][c] = sum over the positions k of split
+// ks of a16[t][k] * w_down_t[idx[k]][c].
 struct MmDown {
   const half_t* a16;     // [Bp][lda]
   int lda, B;
@@ -174,53 +207,81 @@ struct MmDown {
   const int32_t* idx;
   const int32_t* n_dev;
   int ffn, d;
-  int ks_len;            // positions per K split (multiple of 16)
+  int ks_len;            // positions per K split (multiple of 16, at most MD_SPLIT_MAX)
   float* part;           // [KS][B][d]
 };
 
-template <int MT>
+// ---------------------------------------------------------------------------------------
+// k_mm_down: the down projection. A wave owns 128 output columns (4 per lane of a half-wave:
+// one 8-byte load per row) and all (up to 64) tokens, and walks its workgroup's K split 32
+// positions per step: lanes of half h load rows k + 8h .. k + 8h + 7 (and the same of the
+// next 16), so each lane holds the 8 K values of its 4 columns and feeds four MFMAs whose
+// output columns are {4*(l%32) + j}. Both 16-position steps' rows and activations are in
+// flight together; the split's index list is staged in LDS first.
+// ---------------------------------------------------------------------------------------
+constexpr int MD_SPLIT_MAX = 4096;  // positions of one K split
+
 __global__ __launch_bounds__(BLOCK) void k_mm_down(MmDown p) {
+  constexpr int MT = 2;  // 64 token rows
+  __shared__ int s_idx[MD_SPLIT_MAX];
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int n = min(max(*p.n_dev, 0), p.ffn);
   const int c0 = (blockIdx.x * NWAVES + wave) * 128 + 4 * (lane & 31);
   const bool cvalid = c0 < p.d;
   const int kh = 8 * (lane >> 5);
-  const int k_begin = blockIdx.y * p.ks_len, k_end = min(n, k_begin + p.ks_len);
+  const int k_begin = blockIdx.y * p.ks_len;
+  const int len = max(0, min(n, k_begin + p.ks_len) - k_begin);  // <= ks_len <= MD_SPLIT_MAX
+  for (int j = threadIdx.x; j < len; j += BLOCK) {
+    const int i = p.idx[k_begin + j];
+    s_idx[j] = ((unsigned)i < (unsigned)p.ffn) ? i : -1;
+  }
+  __syncthreads();
   f16v acc[MT][4];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = (f16v){};
-  for (int k = k_begin; k < k_end; k += 16) {
-    uint32_t lo[8], hi[8];
+  for (int k = 0; k < len; k += 32) {
+    uint64_t v[2][8];
+    h8 a[2][MT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int kk = k + kh + e;
-      int i = (kk < k_end) ? p.idx[kk] : -1;
-      if ((unsigned)i >= (unsigned)p.ffn) i = -1;
-      uint64_t v = 0;
-      if (i >= 0 && cvalid) v = *reinterpret_cast<const uint64_t*>(p.wd + (size_t)i * p.d + c0);
-      lo[e] = (uint32_t)v;
-      hi[e] = (uint32_t)(v >> 32);
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = k + 16 * st + kh + e;
+        const int i = (kk < len) ? s_idx[kk] : -1;
+        v[st][e] = (i >= 0 && cvalid) ? *reinterpret_cast<const uint64_t*>(p.wd + (size_t)i * p.d + c0) : 0ull;
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int t = 32 * m + (lane & 31);
+        // a step past the split's end loads nothing (its positions would run past lda)
+        a[st][m] = (k + 16 * st < len && t < p.B)
+                       ? __builtin_bit_cast(h8, ld16(p.a16 + (size_t)t * p.lda + k_begin + k + 16 * st + kh))
+                       : (h8){};
+      }
     }
-    h8 bj[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const half2_t l2 = __builtin_bit_cast(half2_t, lo[e]), h2 = __builtin_bit_cast(half2_t, hi[e]);
-      bj[0][e] = l2.x;
-      bj[1][e] = l2.y;
-      bj[2][e] = h2.x;
-      bj[3][e] = h2.y;
-    }
+    for (int st = 0; st < 2; ++st) {
+      if (k + 16 * st >= len) break;
+      h8 bj[4];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int t = 32 * m + (lane & 31);
-      h8 a = __builtin_bit_cast(h8, ld16(p.a16 + (size_t)t * p.lda + k + kh));
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (uint32_t)v[st][e], hi = (uint32_t)(v[st][e] >> 32);
+        bj[0][e] = __builtin_bit_cast(half_t, (uint16_t)(lo & 0xFFFFu));
+        bj[1][e] = __builtin_bit_cast(half_t, (uint16_t)(lo >> 16));
+        bj[2][e] = __builtin_bit_cast(half_t, (uint16_t)(hi & 0xFFFFu));
+        bj[3][e] = __builtin_bit_cast(half_t, (uint16_t)(hi >> 16));
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k + kh + e >= k_end) a[e] = (half_t)0.f;
+      for (int m = 0; m < MT; ++m) {
+        h8 av = a[st][m];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][j] = mfma(a, bj[j], acc[m][j]);
+        for (int e = 0; e < 8; ++e)
+          if (k + 16 * st + kh + e >= len) av[e] = (half_t)0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = mfma(av, bj[j], acc[m][j]);
+      }
     }
   }
   if (!cvalid) return;
