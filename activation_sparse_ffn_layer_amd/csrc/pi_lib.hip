@@ -482,8 +482,8 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   q.ffn = L.ffn;
   q.d = L.d;
   // K splits: enough workgroups to fill the chip, each split at most MD_SPLIT_MAX positions
-  const int cblocks = (L.d + 511) / 512;
-  int ks = std::min(MM_KSD, std::max((512 + cblocks - 1) / cblocks, (L.ffn + MD_SPLIT_MAX - 1) / MD_SPLIT_MAX));
+  const int cblocks = (L.d + MD_COLS - 1) / MD_COLS;
+  int ks = std::min(MM_KSD, std::max((1024 + cblocks - 1) / cblocks, (L.ffn + MD_SPLIT_MAX - 1) / MD_SPLIT_MAX));
   q.ks_len = ((L.ffn + ks - 1) / ks + 15) / 16 * 16;
   if (q.ks_len > MD_SPLIT_MAX) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the batched path", L.ffn);
   ks = (L.ffn + q.ks_len - 1) / q.ks_len;

@@ -212,21 +212,24 @@ struct MmDown {
 };
 
 // ---------------------------------------------------------------------------------------
-// k_mm_down: the down projection. A wave owns 128 output columns (4 per lane of a half-wave:
-// one 8-byte load per row) and all (up to 64) tokens, and walks its workgroup's K split 32
-// positions per step: lanes of half h load rows k + 8h .. k + 8h + 7 (and the same of the
-// next 16), so each lane holds the 8 K values of its 4 columns and feeds four MFMAs whose
-// output columns are {4*(l%32) + j}. Both 16-position steps' rows and activations are in
-// flight together; the split's index list is staged in LDS first.
+// k_mm_down: the down projection. A pair of waves owns 128 output columns (4 per lane of a
+// half-wave: one 8-byte load per row); wave w takes tokens 32*(w&1).. of them, so each wave
+// holds 32 x 128 accumulators. It walks its workgroup's K split 32 positions per step: lanes
+// of half h load rows k + 8h .. k + 8h + 7 (and the same of the next 16), so each lane holds
+// the 8 K values of its 4 columns and feeds four MFMAs whose output columns are {4*(l%32) + j}.
+// Both 16-position steps' rows and activations are in flight together; the split's index
+// list is staged in LDS first. (The two waves of a pair read the same rows: the second read
+// is served by the caches.)
 // ---------------------------------------------------------------------------------------
 constexpr int MD_SPLIT_MAX = 4096;  // positions of one K split
+constexpr int MD_COLS = 256;        // output columns per workgroup
 
 __global__ __launch_bounds__(BLOCK) void k_mm_down(MmDown p) {
-  constexpr int MT = 2;  // 64 token rows
   __shared__ int s_idx[MD_SPLIT_MAX];
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int n = min(max(*p.n_dev, 0), p.ffn);
-  const int c0 = (blockIdx.x * NWAVES + wave) * 128 + 4 * (lane & 31);
+  const int c0 = blockIdx.x * MD_COLS + (wave >> 1) * 128 + 4 * (lane & 31);
+  const int t = 32 * (wave & 1) + (lane & 31);  // this lane's token row of the A operand
   const bool cvalid = c0 < p.d;
   const int kh = 8 * (lane >> 5);
   const int k_begin = blockIdx.y * p.ks_len;
@@ -236,14 +239,12 @@ __global__ __launch_bounds__(BLOCK) void k_mm_down(MmDown p) {
     s_idx[j] = ((unsigned)i < (unsigned)p.ffn) ? i : -1;
   }
   __syncthreads();
-  f16v acc[MT][4];
+  f16v acc[4];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = (f16v){};
-  for (int k = 0; k < len; k += 32) {
-    uint64_t v[2][8];
-    h8 a[2][MT];
+  for (int j = 0; j < 4; ++j) acc[j] = (f16v){};
+  // 32 positions (two 16-position MFMA steps) per block; blocks are ping-ponged between two
+  // register sets so the next block's rows are in flight while the current one is used
+  auto load = [&](uint64_t (&v)[2][8], h8 (&a)[2], int k) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -252,15 +253,13 @@ __global__ __launch_bounds__(BLOCK) void k_mm_down(MmDown p) {
         const int i = (kk < len) ? s_idx[kk] : -1;
         v[st][e] = (i >= 0 && cvalid) ? *reinterpret_cast<const uint64_t*>(p.wd + (size_t)i * p.d + c0) : 0ull;
       }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int t = 32 * m + (lane & 31);
-        // a step past the split's end loads nothing (its positions would run past lda)
-        a[st][m] = (k + 16 * st < len && t < p.B)
-                       ? __builtin_bit_cast(h8, ld16(p.a16 + (size_t)t * p.lda + k_begin + k + 16 * st + kh))
-                       : (h8){};
-      }
+      // a step past the split's end loads nothing (its positions would run past lda)
+      a[st] = (k + 16 * st < len && t < p.B)
+                  ? __builtin_bit_cast(h8, ld16(p.a16 + (size_t)t * p.lda + k_begin + k + 16 * st + kh))
+                  : (h8){};
     }
+  };
+  auto use = [&](const uint64_t (&v)[2][8], const h8 (&a)[2], int k) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       if (k + 16 * st >= len) break;
@@ -273,28 +272,32 @@ __global__ __launch_bounds__(BLOCK) void k_mm_down(MmDown p) {
         bj[2][e] = __builtin_bit_cast(half_t, (uint16_t)(hi & 0xFFFFu));
         bj[3][e] = __builtin_bit_cast(half_t, (uint16_t)(hi >> 16));
       }
+      h8 av = a[st];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        h8 av = a[st][m];
+      for (int e = 0; e < 8; ++e)
+        if (k + 16 * st + kh + e >= len) av[e] = (half_t)0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k + 16 * st + kh + e >= len) av[e] = (half_t)0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = mfma(av, bj[j], acc[m][j]);
-      }
+      for (int j = 0; j < 4; ++j) acc[j] = mfma(av, bj[j], acc[j]);
     }
+  };
+  uint64_t v0[2][8], v1[2][8];
+  h8 a0[2], a1[2];
+  if (len > 0) load(v0, a0, 0);
+  for (int k = 0; k < len; k += 64) {
+    if (k + 32 < len) load(v1, a1, k + 32);
+    use(v0, a0, k);
+    if (k + 64 < len) load(v0, a0, k + 64);
+    if (k + 32 < len) use(v1, a1, k + 32);
   }
   if (!cvalid) return;
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * m + mfma_row(r, lane);
-      if (t < p.B) {
-        float* o = p.part + ((size_t)blockIdx.y * p.B + t) * p.d + c0;
-        *reinterpret_cast<f32x4*>(o) = (f32x4){acc[m][0][r], acc[m][1][r], acc[m][2][r], acc[m][3][r]};
-      }
+  for (int r = 0; r < 16; ++r) {
+    const int tr = 32 * (wave & 1) + mfma_row(r, lane);
+    if (tr < p.B) {
+      float* o = p.part + ((size_t)blockIdx.y * p.B + tr) * p.d + c0;
+      *reinterpret_cast<f32x4*>(o) = (f32x4){acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
     }
+  }
 }
 
 // z = sum of G partials [G][B][N], written as fp16 hi and lo halves (z = hi + lo to ~22 bits).
