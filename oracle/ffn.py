@@ -26,6 +26,7 @@ What the method computes, per FFN layer and token x (all in float64 here):
    row and column vectors):
    ReLU ``a_i = max(W_up[i] . x + b_i, 0)``;
    ReGLU ``a_i = max(W_gate[i] . x + b_i, 0) * (W_up[i] . x)``;
+   Squared-ReLU ``a_i = max(W_up[i] . x + b_i, 0) ** 2``;
    ``y = sum_i a_i * W_down[:, i]`` (stored neuron-major as ``w_down_t[i]``).
    P1 (header bullets, «Kısıtlar ve SSS») restricts the method to ReLU / ReGLU
    / Squared-ReLU models.
@@ -44,6 +45,8 @@ Readings taken where the pages are silent (each is a named choice):
 * A batch uses the union of its tokens' masks for every token; ReLU zeroes
   the neurons a token does not itself activate.
 * ReGLU: only the gate has a bias; the mask is taken on the gate.
+* Squared-ReLU (named, not defined, by the pages): ``max(h, 0) ** 2`` of the up
+  projection; like ReLU it has one row per neuron and the mask is taken on it.
 * Layers of a stack are chained by ``x_next = fp16(y / rms(y))`` (the pages
   give no layer between FFNs); an all-zero y passes x through unchanged.
 * Decision values within 1e-4 of theta form an exclusion band: there a
@@ -89,7 +92,7 @@ def rows_f64(layer: dict, which: str, rows=None) -> np.ndarray:
 
 
 def _masked_name(layer: dict) -> str:
-    return "up" if layer["act"] == "relu" else "gate"
+    return "gate" if layer["act"] == "reglu" else "up"
 
 
 # ------------------------------------------------------------------------------------------
@@ -172,6 +175,9 @@ def sparse_ffn(layer: dict, x: np.ndarray, idx: np.ndarray, chunk: int = 2048) -
         if layer["act"] == "relu":
             h = x64 @ rows_f64(layer, "up", rows).T + b[rows]
             a = np.maximum(h, 0.0)
+        elif layer["act"] == "sqrelu":
+            h = x64 @ rows_f64(layer, "up", rows).T + b[rows]
+            a = np.maximum(h, 0.0) ** 2
         elif layer["act"] == "reglu":
             g = x64 @ rows_f64(layer, "gate", rows).T + b[rows]
             u = x64 @ rows_f64(layer, "up", rows).T

@@ -41,7 +41,7 @@ class StackConfig:
     d: int
     ffn: int
     wtype: str                 # "f32" | "f16" | "q4_0"
-    act: str                   # "relu" | "reglu"
+    act: str                   # "relu" | "reglu" | "sqrelu"
     rank: Optional[int]        # None: no predictor (true mask); -1: adaptive per layer
     mean_active: Tuple[float, float]   # (lo, hi); lo == hi for a fixed mean
     alpha: Optional[float]     # None: solve for the mass share below

@@ -282,7 +282,7 @@ def make_layer(cfg: StackConfig, layer: int, master: int = 0, device="cpu") -> L
     del w_down
     pl_w, pl_s = store(w_plain)
     del w_plain
-    if cfg.act == "relu":
+    if cfg.act in ("relu", "sqrelu"):
         up, s_up, gate, s_gate = m_w, m_s, None, None
     elif cfg.act == "reglu":
         up, s_up, gate, s_gate = pl_w, pl_s, m_w, m_s

@@ -51,6 +51,20 @@ def test_golden_relu_tiny():
     np.testing.assert_array_equal(r["y"], g["y_union"])
 
 
+def test_golden_sqrelu_tiny():
+    g = _golden("sqrelu_tiny.json")
+    L = _layer_dict("sqrelu", g["w_up"], g["b"], g["w_down_t"])
+    x = np.array(g["x"], dtype=np.float64)
+    m = oracle.threshold(oracle.decision_values(L, x))
+    np.testing.assert_array_equal(m, g["mask"])
+    for t in range(2):
+        y = oracle.sparse_ffn(L, x[t], oracle.compact(m[t]))
+        np.testing.assert_array_equal(y[0], g["y_per_token"][t])
+    r = oracle.layer_forward(L, x)
+    np.testing.assert_array_equal(r["idx"], g["union_idx"])
+    np.testing.assert_array_equal(r["y"], g["y_union"])
+
+
 def test_golden_reglu_tiny():
     g = _golden("reglu_tiny.json")
     L = _layer_dict("reglu", g["w_up"], g["b"], g["w_down_t"], w_gate=g["w_gate"])
@@ -189,6 +203,13 @@ def _dense_relu(L, x):
     return (W_down @ np.maximum(W_up @ x + L["b"], 0.0))
 
 
+def _dense_sqrelu(L, x):
+    """Textbook dense Squared-ReLU FFN: W_down relu(W_up x + b)^2."""
+    W_up = np.asarray(L["w_up"], dtype=np.float64)
+    W_down = np.asarray(L["w_down_t"], dtype=np.float64).T
+    return W_down @ np.square(np.maximum(W_up @ x + L["b"], 0.0))
+
+
 def _dense_reglu(L, x):
     Wg = np.asarray(L["w_gate"], dtype=np.float64)
     Wu = np.asarray(L["w_up"], dtype=np.float64)
@@ -205,6 +226,23 @@ def test_true_mask_sparse_equals_dense_relu(wtype):
         r = oracle.layer_forward(L, x[None])
         assert 0 < r["n_active"] < L["ffn"]
         np.testing.assert_allclose(r["y"][0], _dense_relu(L, x), rtol=0, atol=1e-12)
+
+
+def test_true_mask_sparse_equals_dense_sqrelu():
+    rng = np.random.default_rng(12)
+    L = _random_layer(rng, "sqrelu")
+    for _ in range(8):
+        x = rng.normal(size=64)
+        r = oracle.layer_forward(L, x[None])
+        assert 0 < r["n_active"] < L["ffn"]
+        np.testing.assert_allclose(r["y"][0], _dense_sqrelu(L, x), rtol=0, atol=1e-12)
+    # a single neuron gives h_i^2 w_down_t[i]; a listed inactive neuron gives nothing
+    x = rng.normal(size=64)
+    h = np.asarray(L["w_up"]) @ x + L["b"]
+    i, j = int(np.argmax(h)), int(np.argmin(h))
+    np.testing.assert_allclose(oracle.sparse_ffn(L, x, np.array([i]))[0], h[i] ** 2 * np.asarray(L["w_down_t"])[i],
+                               rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(oracle.sparse_ffn(L, x, np.array([j]))[0], np.zeros(64))
 
 
 def test_true_mask_sparse_equals_dense_reglu():
@@ -235,11 +273,11 @@ def test_all_active_empty_and_single_neuron():
 def test_batch_union_equals_per_token_equals_dense():
     """With the true mask, the union over a batch gives each token its own dense FFN."""
     rng = np.random.default_rng(4)
-    for act in ("relu", "reglu"):
+    for act in ("relu", "reglu", "sqrelu"):
         L = _random_layer(rng, act)
         X = rng.normal(size=(8, 64))
         r = oracle.layer_forward(L, X)
-        dense = _dense_relu if act == "relu" else _dense_reglu
+        dense = {"relu": _dense_relu, "reglu": _dense_reglu, "sqrelu": _dense_sqrelu}[act]
         for t in range(8):
             np.testing.assert_allclose(r["y"][t], dense(L, X[t]), atol=1e-12)
             own = oracle.layer_forward(L, X[t][None])
