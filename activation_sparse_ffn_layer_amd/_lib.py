@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpi.so")
 
 PI_OK, PI_ERR_INVALID, PI_ERR_UNSUPPORTED, PI_ERR_OOM, PI_ERR_HIP = range(5)
 KERNEL_CLASSES = ("stage1", "stage2", "truemask", "up", "down", "reduce")
-ACT = {"relu": 0, "reglu": 1}
+ACT = {"relu": 0, "reglu": 1, "sqrelu": 2}
 WTYPE = {"f32": 0, "f16": 1, "q4_0": 2}
 
 

@@ -25,7 +25,19 @@
 namespace pi {
 
 enum { W_F32 = 0, W_F16 = 1, W_Q4 = 2 };
-enum { ACT_RELU = 0, ACT_REGLU = 1 };
+enum { ACT_RELU = 0, ACT_REGLU = 1, ACT_SQRELU = 2 };
+
+// Activation of a one-row family (ReLU, Squared-ReLU) from its pre-activation h.
+template <int ACT>
+__device__ __forceinline__ float act_one(float h) {
+  const float r = fmaxf(h, 0.f);
+  if constexpr (ACT == ACT_SQRELU) return r * r;
+  else return r;
+}
+__device__ __forceinline__ float act_one_rt(int act, float h) {
+  const float r = fmaxf(h, 0.f);
+  return (act == ACT_SQRELU) ? r * r : r;
+}
 
 struct LayerDev {
   int d, ffn, rank, act, wtype;
@@ -347,19 +359,19 @@ template <int WT, int R> struct ActU {
 };
 
 constexpr int ACT_RA = 4;  // rows in flight per wave in a round
-template <int ACT> struct ActPW { static constexpr int PW = (ACT == ACT_RELU) ? 4 : 2; };
+template <int ACT> struct ActPW { static constexpr int PW = (ACT == ACT_REGLU) ? 2 : 4; };
 
 // acc[r][t] += row_r[c0, c0+cw) . xs[t][0, cw) for the rows of the first NR ids.
 template <int WT, int ACT, int NB, int NR, typename XT>
 __device__ __forceinline__ void act_accum(const LayerDev& L, const XT* xs, int ldx, int c0, int cw, int lane,
                                           const int (&ids)[ActPW<ACT>::PW], float (&acc)[ACT_RA][NB]) {
-  constexpr int R = (ACT == ACT_RELU ? 1 : 2) * NR;
+  constexpr int R = (ACT == ACT_REGLU ? 2 : 1) * NR;
   const int d = L.d;
   const uint8_t* rows[ACT_RA] = {nullptr, nullptr, nullptr, nullptr};
   const uint16_t* srows[ACT_RA] = {nullptr, nullptr, nullptr, nullptr};
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
-    if constexpr (ACT == ACT_RELU) {
+    if constexpr (ACT != ACT_REGLU) {
       rows[q] = row_at<WT>(L.w_up, ids[q], d, c0);
       srows[q] = scale_at<WT>(L.s_up, ids[q], d, c0);
     } else {
@@ -383,8 +395,8 @@ __device__ __forceinline__ void act_store(const LayerDev& L, int B, int lane, co
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
         float v;
-        if constexpr (ACT == ACT_RELU) {
-          v = fmaxf(wave_sum(acc[q][t]) + bias, 0.f);
+        if constexpr (ACT != ACT_REGLU) {
+          v = act_one<ACT>(wave_sum(acc[q][t]) + bias);
         } else {
           const float g = wave_sum(acc[2 * q][t]) + bias;
           const float u = wave_sum(acc[2 * q + 1][t]);
@@ -424,7 +436,7 @@ __device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const 
         stage(c0, cw);
         __syncthreads();
       }
-      if constexpr (ACT == ACT_RELU) {
+      if constexpr (ACT != ACT_REGLU) {
         switch (m) {
           case 1: act_accum<WT, ACT, NB, 1, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
           case 2: act_accum<WT, ACT, NB, 2, XT>(L, xs, ldx, c0, cw, lane, ids, acc); break;
@@ -699,8 +711,8 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
   if (xin.y != nullptr) glue_x<NB, XT>(xin, B, d, xs, d, red, blockIdx.x == 0);
   else load_x_cols<NB, XT>(xin.x, B, d, 0, d, xs, d);
   __syncthreads();
-  const uint8_t* W = (L.act == ACT_RELU) ? L.w_up : L.w_gate;
-  const uint16_t* S = (L.act == ACT_RELU) ? L.s_up : L.s_gate;
+  const uint8_t* W = (L.act == ACT_REGLU) ? L.w_gate : L.w_up;
+  const uint16_t* S = (L.act == ACT_REGLU) ? L.s_gate : L.s_up;
   // Rows here are d long, so one full wave reduction per row costs little next to its loads.
 #pragma unroll 1
   for (int i = 0; i < 16; i += 2) {
@@ -723,12 +735,12 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
   if (wave == 0) {
     const uint64_t u = emit_mask<NB>(vs, tile, B, L.threshold, ffn, mask_tok, mask_union, logits);
     if constexpr (UP) {
-      if (L.act == ACT_RELU) {
-        // a = max(h, 0) for the union's neurons (a token's inactive neurons give 0)
+      if (L.act != ACT_REGLU) {
+        // a = act(h) for the union's neurons (a token's inactive neurons give 0)
         if ((u >> lane) & 1ull)
 #pragma unroll
           for (int t = 0; t < NB; ++t)
-            if (t < B) a[(size_t)t * ffn + tile * WAVE + lane] = fmaxf(vs[t][lane], 0.f);
+            if (t < B) a[(size_t)t * ffn + tile * WAVE + lane] = act_one_rt(L.act, vs[t][lane]);
       }
     }
     if (lane == 0) s_union = u;

@@ -118,6 +118,8 @@ hipError_t launch_k(pi_ctx* c, int klass, void (*kern)(P...), dim3 grid, size_t 
 }
 enum { K_STAGE1 = 0, K_STAGE2, K_TRUEMASK, K_UP, K_DOWN, K_REDUCE, K_COUNT };
 static_assert(K_COUNT == PI_KERNEL_CLASSES, "kernel classes out of sync with pi.h");
+static_assert(PI_ACT_RELU == ACT_RELU && PI_ACT_REGLU == ACT_REGLU && PI_ACT_SQRELU == ACT_SQRELU,
+              "activation codes out of sync with pi.h");
 
 LayerDev to_dev(const pi_ffn_desc& d) {
   LayerDev L;
@@ -201,13 +203,19 @@ pi_status launch_stage2_t(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, f
 template <int NB, int CPL>
 pi_status launch_stage2_c(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
   if (x == nullptr) return launch_stage2_t<NB, CPL, false, W_F16, ACT_RELU>(c, L, B, mtok, logits, x);
-  if (L.wtype == W_F16)
-    return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_F16, ACT_RELU>(c, L, B, mtok, logits, x)
-                             : launch_stage2_t<NB, CPL, true, W_F16, ACT_REGLU>(c, L, B, mtok, logits, x);
-  if (L.wtype == W_Q4)
-    return L.act == ACT_RELU ? launch_stage2_t<NB, CPL, true, W_Q4, ACT_RELU>(c, L, B, mtok, logits, x)
-                             : launch_stage2_t<NB, CPL, true, W_Q4, ACT_REGLU>(c, L, B, mtok, logits, x);
-  return fail(c, PI_ERR_UNSUPPORTED, "no predictor path for this weight type");
+  if (L.wtype != W_F16 && L.wtype != W_Q4) return fail(c, PI_ERR_UNSUPPORTED, "no predictor path for this weight type");
+  if (L.wtype == W_F16) {
+    switch (L.act) {
+      case ACT_RELU: return launch_stage2_t<NB, CPL, true, W_F16, ACT_RELU>(c, L, B, mtok, logits, x);
+      case ACT_REGLU: return launch_stage2_t<NB, CPL, true, W_F16, ACT_REGLU>(c, L, B, mtok, logits, x);
+      default: return launch_stage2_t<NB, CPL, true, W_F16, ACT_SQRELU>(c, L, B, mtok, logits, x);
+    }
+  }
+  switch (L.act) {
+    case ACT_RELU: return launch_stage2_t<NB, CPL, true, W_Q4, ACT_RELU>(c, L, B, mtok, logits, x);
+    case ACT_REGLU: return launch_stage2_t<NB, CPL, true, W_Q4, ACT_REGLU>(c, L, B, mtok, logits, x);
+    default: return launch_stage2_t<NB, CPL, true, W_Q4, ACT_SQRELU>(c, L, B, mtok, logits, x);
+  }
 }
 
 template <int NB>
@@ -283,18 +291,20 @@ pi_status launch_up_a(pi_ctx* c, const LayerDev& L, const void* x, int B, const 
   }
 }
 
-pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
-  if (L.act == ACT_RELU) {
-    switch (L.wtype) {
-      case W_F32: return launch_up_a<W_F32, ACT_RELU>(c, L, x, B, idx_in, n_in);
-      case W_F16: return launch_up_a<W_F16, ACT_RELU>(c, L, x, B, idx_in, n_in);
-      default: return launch_up_a<W_Q4, ACT_RELU>(c, L, x, B, idx_in, n_in);
-    }
-  }
+template <int ACT>
+pi_status launch_up_w(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
   switch (L.wtype) {
-    case W_F32: return launch_up_a<W_F32, ACT_REGLU>(c, L, x, B, idx_in, n_in);
-    case W_F16: return launch_up_a<W_F16, ACT_REGLU>(c, L, x, B, idx_in, n_in);
-    default: return launch_up_a<W_Q4, ACT_REGLU>(c, L, x, B, idx_in, n_in);
+    case W_F32: return launch_up_a<W_F32, ACT>(c, L, x, B, idx_in, n_in);
+    case W_F16: return launch_up_a<W_F16, ACT>(c, L, x, B, idx_in, n_in);
+    default: return launch_up_a<W_Q4, ACT>(c, L, x, B, idx_in, n_in);
+  }
+}
+
+pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx_in, const int32_t* n_in) {
+  switch (L.act) {
+    case ACT_RELU: return launch_up_w<ACT_RELU>(c, L, x, B, idx_in, n_in);
+    case ACT_REGLU: return launch_up_w<ACT_REGLU>(c, L, x, B, idx_in, n_in);
+    default: return launch_up_w<ACT_SQRELU>(c, L, x, B, idx_in, n_in);
   }
 }
 
@@ -444,7 +454,7 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
   p.x = x;
   p.K = L.d;
   p.ldx = L.d;
-  p.w0 = reinterpret_cast<const half_t*>(L.act == ACT_RELU ? L.w_up : L.w_gate);
+  p.w0 = reinterpret_cast<const half_t*>(L.act == ACT_REGLU ? L.w_gate : L.w_up);
   p.N = L.ffn;
   p.ks_len = L.d;
   p.bias = L.b;
@@ -461,7 +471,7 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   p.B = B;
   p.K = L.d;
   p.ldx = L.d;
-  p.w0 = reinterpret_cast<const half_t*>(L.act == ACT_RELU ? L.w_up : L.w_gate);
+  p.w0 = reinterpret_cast<const half_t*>(L.act == ACT_REGLU ? L.w_gate : L.w_up);
   p.w1 = reinterpret_cast<const half_t*>(L.w_up);
   p.idx = idx;
   p.n_dev = n;
@@ -470,8 +480,11 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   p.a16 = c->a16;
   p.lda = c->lda;
   p.ffn = L.ffn;
-  if (L.act == ACT_RELU) PI_TRY((launch_mm<EPI_ACT, ACT_RELU, false>(c, p, L.ffn, 1, K_UP)));
-  else PI_TRY((launch_mm<EPI_ACT, ACT_REGLU, false>(c, p, L.ffn, 1, K_UP)));
+  switch (L.act) {
+    case ACT_RELU: PI_TRY((launch_mm<EPI_ACT, ACT_RELU, false>(c, p, L.ffn, 1, K_UP))); break;
+    case ACT_REGLU: PI_TRY((launch_mm<EPI_ACT, ACT_REGLU, false>(c, p, L.ffn, 1, K_UP))); break;
+    default: PI_TRY((launch_mm<EPI_ACT, ACT_SQRELU, false>(c, p, L.ffn, 1, K_UP))); break;
+  }
   MmDown q{};
   q.a16 = c->a16;
   q.lda = c->lda;
@@ -672,7 +685,8 @@ pi_status pi_ffn_create(pi_ctx* ctx, const pi_ffn_desc* desc, pi_ffn** out) {
   if (d.d > ctx->max_d || d.ffn > ctx->max_ffn || d.rank > ctx->max_rank)
     return fail(ctx, PI_ERR_INVALID, "layer %dx%d rank %d exceeds the context (%dx%d rank %d)", d.d, d.ffn, d.rank,
                 ctx->max_d, ctx->max_ffn, ctx->max_rank);
-  if (d.act != PI_ACT_RELU && d.act != PI_ACT_REGLU) return fail(ctx, PI_ERR_INVALID, "unknown activation %d", d.act);
+  if (d.act != PI_ACT_RELU && d.act != PI_ACT_REGLU && d.act != PI_ACT_SQRELU)
+    return fail(ctx, PI_ERR_INVALID, "unknown activation %d", d.act);
   if (d.wtype != PI_W_F32 && d.wtype != PI_W_F16 && d.wtype != PI_W_Q4_0)
     return fail(ctx, PI_ERR_INVALID, "unknown weight type %d", d.wtype);
   if (d.wtype == PI_W_Q4_0 && d.d % 32) return fail(ctx, PI_ERR_INVALID, "Q4_0 needs d %% 32 == 0 (got %d)", d.d);

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(BLOCK) void k_mm_gemm(MmRows p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * tb + mfma_row(r, lane);
-        const float a = (valid && t < p.B) ? fmaxf(acc[r] + bias, 0.f) : 0.f;
+        const float a = (valid && t < p.B) ? act_one<ACT>(acc[r] + bias) : 0.f;
         if (t < p.B) p.a16[(size_t)t * p.lda + col] = (half_t)a;
       }
     }

@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--config", default="opt6.7b")
     ap.add_argument("--batch", type=int, default=None, help="tokens per step (default: the workload's first batch)")
     ap.add_argument("--layers", type=int, default=None, help="override the stack depth (exploration only)")
+    ap.add_argument("--act", choices=["relu", "reglu", "sqrelu"], default=None,
+                    help="override the workload's activation family (e.g. the Squared-ReLU variant)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-steps", type=int, default=16, help="steps of the per-kernel event pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -81,6 +83,26 @@ def recorded_traffic(workload, kernel):
             except ValueError:
                 return None
     return None
+
+
+def stream_read_gbs(seconds_budget=0.5):
+    """Achievable HBM read bandwidth of this GPU: a sum over a 2 GiB fp32 buffer (torch's
+    reduction reads each byte once), best of a few runs, timed with events."""
+    import torch
+    buf = torch.ones((1 << 29,), dtype=torch.float32, device="cuda")  # 2 GiB
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    buf.sum()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        e0.record()
+        buf.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del buf
+    torch.cuda.empty_cache()
+    return (1 << 31) / best / 1e9
 
 
 def calibrate_copy():
@@ -134,7 +156,7 @@ def kernel_bytes(cls, L, B, n_list):
     w = WBYTES[L.wtype]
     xe = 4 if L.wtype == "f32" else 2
     d, F, r = L.d, L.ffn, L.rank
-    k_up = 1 if L.act == "relu" else 2
+    k_up = 2 if L.act == "reglu" else 1
     if B > 8:
         if cls == "stage1":
             return len(n_list) * (r * d * 2 + B * d * 2 + B * r * 4)
@@ -223,6 +245,8 @@ def main():
     cfg = CONFIGS[args.config]
     if args.layers:
         cfg = dataclasses.replace(cfg, layers=args.layers)
+    if args.act:
+        cfg = dataclasses.replace(cfg, act=args.act)
     B = args.batch if args.batch else cfg.batches[0]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -293,6 +317,10 @@ def main():
                 "traffic": None if traffic is None else round(traffic),
                 "bytes_per_launch": round(bytes_per_launch), "avg_launch_us": round(1e3 * dms / dcnt, 3)}
 
+    stream_gbs = stream_read_gbs()
+    log(f"stream read: {stream_gbs:.0f} GB/s achievable; the path moves "
+        f"{active_bytes / elapsed_s / 1e9:.0f} GB/s of active bytes")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layers, xt, B, args.cpu_seconds)
@@ -306,6 +334,8 @@ def main():
                    "ffn": cfg.ffn, "rank": cfg.rank, "weights": cfg.wtype, "batch": B, "seed": args.seed,
                    "hot_first": cfg.hot_first, "graph": use_graph},
         "hbm_frac_active": round(frac_active, 4),
+        "stream_read_gbs": round(stream_gbs, 1),
+        "frac_of_stream_read": round(active_bytes / elapsed_s / 1e9 / stream_gbs, 4),
         "active_mb_per_step": round(active_bytes / args.steps / 1e6, 2),
         "mean_active": round(float(nl.mean()) / cfg.ffn, 4),
         "roofline": roofline,

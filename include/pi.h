@@ -45,8 +45,11 @@ typedef enum {
   PI_ERR_HIP = 4           /* a HIP runtime call failed; see pi_last_error                    */
 } pi_status;
 
-/* Activation families the method supports (P1 header bullets, «Kısıtlar ve SSS»). */
-typedef enum { PI_ACT_RELU = 0, PI_ACT_REGLU = 1 } pi_act;
+/* Activation families the method supports (P1 header bullets, «Kısıtlar ve SSS»):
+ * ReLU a = max(h, 0); ReGLU a = max(g, 0) * u; Squared-ReLU a = max(h, 0)^2. ReLU and
+ * Squared-ReLU read one row per neuron (w_up, masked on h > 0); ReGLU reads two (w_gate,
+ * masked on g > 0, and w_up). */
+typedef enum { PI_ACT_RELU = 0, PI_ACT_REGLU = 1, PI_ACT_SQRELU = 2 } pi_act;
 
 /* Weight storage. PI_W_Q4_0: each block of 32 consecutive elements of a row stores an fp16
  * scale s and 32 4-bit codes q; the weight is (q - 8) * s (P1 «Kuantizasyon ve uyumluluk»).

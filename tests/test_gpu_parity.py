@@ -101,6 +101,13 @@ CASES = {
     "reglu-truemask-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 0, 8, 8),
     "f16-b8-xwindows": (_cfg("opt6.7b", d=12288, ffn=2048, rank=512), 0, 8, 8),
     "opt175-full-q4-b8": (_cfg("opt175b"), 0, 8, 8),
+    # Squared-ReLU (one up row per neuron, a = max(h, 0)^2) on every path
+    "sqrelu-small": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=4096, rank=512), 0, 8, 1),
+    "sqrelu-full": (_cfg("opt6.7b", act="sqrelu"), 2, 2, 1),
+    "sqrelu-b8": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=4096, rank=512), 1, 16, 8),
+    "sqrelu-truemask-b3": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=2048, rank=None), 0, 6, 3),
+    "sqrelu-q4-b2": (_cfg("opt175b", act="sqrelu", d=2048, ffn=4096, rank=512), 0, 4, 2),
+    "sqrelu-b32-mfma": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=4096, rank=512), 2, 32, 32),
     # batched path on the matrix cores (9..64 tokens)
     "relu-b16-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 32, 16),
     "reglu-b64-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 2, 64, 64),
@@ -232,8 +239,9 @@ def test_glue(dtype):
 
 # ------------------------------------------------------------------------------ stacks
 
-def test_stack_true_mask_chain_matches_oracle():
-    cfg = _cfg("opt6.7b", layers=3, d=1024, ffn=4096, rank=None)
+@pytest.mark.parametrize("act", ["relu", "sqrelu"])
+def test_stack_true_mask_chain_matches_oracle(act):
+    cfg = _cfg("opt6.7b", layers=3, d=1024, ffn=4096, rank=None, act=act)
     layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
     X = make_tokens(cfg, 4, device="cuda")
     ctx = make_ctx(layers, max_batch=1)
