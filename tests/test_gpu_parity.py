@@ -356,3 +356,45 @@ def test_stack_batched_graph_equals_eager():
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
     assert torch.all(torch.isfinite(outs[0]))
+
+
+# ---------------------------------------------------------------- stacks at the bench's shapes
+
+STACKS = {
+    # name: (config, layers, tokens, batch)
+    "opt6.7b-b1": (_cfg("opt6.7b", layers=3), 3, 2, 1),
+    "opt175b-q4-b8": (_cfg("opt175b", layers=2), 2, 8, 8),
+    "llama70b-b64": (_cfg("llama70b", layers=2), 2, 64, 64),
+}
+
+
+@pytest.mark.parametrize("case", list(STACKS))
+def test_stack_full_size_graph_equals_eager(case):
+    """Full layer shapes in the launch configuration bench.py times (a HIP graph per step):
+    the graph and eager runs agree bit for bit, the output is finite, and the first layer's
+    union count is the oracle's up to the neurons inside its exclusion band."""
+    cfg, nl, T, B = STACKS[case]
+    _say(f"stack {case}: {nl} layers d={cfg.d} ffn={cfg.ffn} B={B}")
+    layers = [make_layer(cfg, i, device="cuda") for i in range(nl)]
+    X = make_tokens(cfg, T, device="cuda", stream=99)
+    ctx = make_ctx(layers, max_batch=B)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+    outs, logs = [], []
+    for use_graph in (True, False):
+        y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+        nlog = torch.zeros((T // B, nl), dtype=torch.int32, device="cuda")
+        pi.stack_run(ctx, ffns, X, B, y, nlog, use_graph=use_graph)
+        outs.append(y)
+        logs.append(nlog)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "graph and eager runs differ"
+    assert torch.equal(logs[0], logs[1])
+    assert torch.all(torch.isfinite(outs[0]))
+    H0 = layers[0].to_host()
+    for s in range(T // B):
+        xh = X[s * B:(s + 1) * B].cpu().numpy()
+        v = oracle.decision_values(H0, xh)
+        u = oracle.union(oracle.threshold(v, H0["threshold"]))
+        nb = int(oracle.union(oracle.band(v, H0["threshold"])).sum())
+        got = int(logs[0][s, 0].item())
+        assert abs(got - int(u.sum())) <= nb, (got, int(u.sum()), nb)
