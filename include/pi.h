@@ -68,12 +68,12 @@ typedef struct pi_ffn pi_ffn;
  *   rank     predictor rank r (multiple of 8, at most 1024; fp16 / Q4_0 layers only), or 0:
  *            no predictor, the mask is the true pre-activation of the masked projection
  *            (> threshold)
- *   act      pi_act. ReLU masks the up projection; ReGLU masks the gate.
+ *   act      pi_act. ReLU and Squared-ReLU mask the up projection; ReGLU masks the gate.
  *   wtype    pi_wtype of w_up / w_gate / w_down_t
  *   threshold decision threshold on the predictor logit (0 == "sigmoid > 0.5")
- *   w_up, w_gate, w_down_t   [ffn][d] (fp32 / fp16) or Q4_0 codes; w_gate NULL for ReLU
+ *   w_up, w_gate, w_down_t   [ffn][d] (fp32 / fp16) or Q4_0 codes; w_gate NULL unless ReGLU
  *   s_up, s_gate, s_down     Q4_0 fp16 scales [ffn][d/32]; NULL otherwise
- *   b        fp32 [ffn] bias of the masked projection (up for ReLU, gate for ReGLU)
+ *   b        fp32 [ffn] bias of the masked projection (gate for ReGLU, else up)
  *   p_w1     fp16 [rank][d], p_w2 fp16 [ffn][rank], p_b fp32 [ffn]: the low-rank predictor
  *            logit = p_w2 (p_w1 x) + p_b (P3 «Prediktor Kepadatan Adaptif»); NULL if rank 0
  *   neuron_table  int32 [ffn] stored row -> original neuron id, or NULL (identity).
@@ -162,10 +162,11 @@ pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, cons
 
 /* Kernel classes of pi_stack_profile's outputs, in this order:
  * predictor stage 1 (with the glue); predictor stage 2 + threshold + the activations of the
- * workgroup's own active neurons; true-mask threshold GEMV + activations; gathered up/gate
- * GEMV of the index-list entry point; down projection (with the index scan) into partial
- * sums that the last workgroup of each column slice adds into y; the separate reduction
- * kernels of the matrix-core path (partial sums, compaction, predictor hi/lo split). */
+ * workgroup's active neurons; true-mask threshold GEMV + activations; gathered up/gate GEMV
+ * (index-list entry point, and the matrix-core path's gathered GEMM); down projection (with
+ * the index scan) into partial sums; the small kernels: sum of partial sums into y, glue
+ * between layers of several tokens, compaction and predictor hi/lo split of the matrix-core
+ * path. */
 #define PI_KERNEL_CLASSES 6
 
 /* pi_stack_run without a graph, every kernel dispatched with a pair of hipEvents
