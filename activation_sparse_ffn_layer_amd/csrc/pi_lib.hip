@@ -870,8 +870,7 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
         const void* x_in = ctx->xstage;
         if (l > 0) {
           const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-          hipLaunchKernelGGL(k_glue<false>, dim3(B), dim3(BLOCK), 0, ctx->stream, ctx->y, x_prev, d, ctx->xbuf[l & 1]);
-          PI_HIP(ctx, hipGetLastError());
+          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
           x_in = ctx->xbuf[l & 1];
         }
         PI_TRY(enqueue_batched(ctx, layers[l], x_in, B, ctx->y, nullptr, ctx->idx, ctx->nbuf, ctx->nlog + l));
