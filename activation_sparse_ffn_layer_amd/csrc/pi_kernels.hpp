@@ -12,10 +12,12 @@
 //   k_down_part  y = sum over active i of a_i w_down_t[i]: every workgroup prefix-scans the
 //                                         mask words itself (no waiting on other workgroups),
 //                                         takes one group of active neurons over one column
-//                                         slice into a partial sum; the last workgroup of a
-//                                         slice adds the partials in a fixed order
-// plus k_up (the index-list entry point's gathered GEMV), k_compact, k_threshold, k_glue,
-// k_reduce (partials of the batched path) and k_permute_rows.
+//                                         slice into a partial sum; the partials are added
+//                                         in a fixed order by k_reduce or the next layer's glue
+// When x of the batch is above 64 KiB, stage 2 stops after the threshold and k_up_cols +
+// k_act_fin compute the activations over column slices of x instead.
+// Plus k_up (the index-list entry point's gathered GEMV), k_compact, k_threshold, k_glue,
+// k_reduce and k_permute_rows.
 //
 // Pages: P3 = "PowerInfer: Mesin Inferensi LLM Cepat dengan GPU Konsumen" (unite.ai),
 // P1 = "Tüketici sınıfı GPU takılı PC'lerde yüksek hızlı büyük dil modeli serving".
@@ -408,12 +410,12 @@ __device__ __forceinline__ void act_store(const LayerDev& L, int B, int lane, co
   }
 }
 
-template <int WT, int ACT, int NB, typename XT, typename IdOf, typename Stage>
-__device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const XT* xs, int ldx, int dw, Stage stage,
-                           float* __restrict__ a) {
+// Rounds over the columns [cb, ce) of the rows; out(ids, m, acc) takes each round's sums.
+template <int WT, int ACT, int NB, typename XT, typename IdOf, typename Stage, typename Out>
+__device__ void act_rounds_cols(const LayerDev& L, int cnt, IdOf id_of, const XT* xs, int ldx, int cb, int ce, int dw,
+                                Stage stage, Out out) {
   constexpr int PW = ActPW<ACT>::PW;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int d = L.d;
   const int rounds = (cnt + NWAVES * PW - 1) / (NWAVES * PW);
   for (int rho = 0; rho < rounds; ++rho) {
     int ids[PW];
@@ -429,9 +431,9 @@ __device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const 
     for (int q = 0; q < ACT_RA; ++q)
 #pragma unroll
       for (int t = 0; t < NB; ++t) acc[q][t] = 0.f;
-    for (int c0 = 0; c0 < d; c0 += dw) {
-      const int cw = min(dw, d - c0);
-      if (dw < d) {
+    for (int c0 = cb; c0 < ce; c0 += dw) {
+      const int cw = min(dw, ce - c0);
+      if (dw < ce - cb) {
         __syncthreads();
         stage(c0, cw);
         __syncthreads();
@@ -452,8 +454,18 @@ __device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const 
         }
       }
     }
-    act_store<ACT, NB>(L, B, lane, ids, m, acc, a);
+    out(ids, m, acc);
   }
+}
+
+template <int WT, int ACT, int NB, typename XT, typename IdOf, typename Stage>
+__device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const XT* xs, int ldx, int dw, Stage stage,
+                           float* __restrict__ a) {
+  const int lane = threadIdx.x % WAVE;
+  auto out = [&](const int (&ids)[ActPW<ACT>::PW], int m, float (&acc)[ACT_RA][NB]) {
+    act_store<ACT, NB>(L, B, lane, ids, m, acc, a);
+  };
+  act_rounds_cols<WT, ACT, NB, XT>(L, cnt, id_of, xs, ldx, 0, L.d, dw, stage, out);
 }
 
 // Copy columns [c0, c0 + cw) of x [NB][d] (rows t >= B zeroed) into xs[t][0, cw) with
@@ -857,6 +869,125 @@ __global__ __launch_bounds__(BLOCK) void k_up(LayerDev L, const void* __restrict
     const int cnt = s_cnt;
     auto id_of = [](int k) { return s_ids[k]; };
     act_rounds<WT, ACT, NB, XT>(L, B, cnt, id_of, xs, xl, xl, stage, a);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// k_up_cols: the gathered up (and gate) GEMV over column slices of x, for batches whose x
+// would leave room for only one workgroup per CU in LDS (every workgroup of the fused
+// kernels stages all of it). Workgroup (s, c) stages the columns [s*sw, s*sw + sw) of x once
+// and takes the list positions [c*P, c*P + P), P = ceil(n / gridDim.y): for each of those
+// neurons i and tokens t, the slice's partial pre-activation row_i[slice] . x_t goes to
+// hp[s][r][t][i] (r = 0: the up row, or for ReGLU 0 = gate, 1 = up). k_act_fin adds the
+// slices in order and applies the activation. The list is the union words' set bits in
+// ascending order (words != nullptr) or the caller's index list (entries outside [0, ffn)
+// skipped). Each partial is computed as in the fused kernels: the lane sums of its chunks,
+// then the wave sum.
+// ---------------------------------------------------------------------------------------
+constexpr int UPC_PMAX = 512;  // list positions per workgroup
+
+template <int WT, int ACT, int NB>
+__global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __restrict__ x, int B, int sw,
+                                                   const uint64_t* __restrict__ words,
+                                                   const int32_t* __restrict__ idx_in,
+                                                   const int32_t* __restrict__ n_in, float* __restrict__ hp) {
+  typedef typename XType<WT == W_F32>::T XT;
+  constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
+  constexpr int PW = ActPW<ACT>::PW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  XT* xs = reinterpret_cast<XT*>(smem);                                         // [NB][sw]
+  int* il = reinterpret_cast<int*>(smem + (size_t)NB * sw * sizeof(XT));        // [UPC_PMAX]
+  __shared__ int red[NWAVES];
+  __shared__ int s_cnt;
+  const int d = L.d, ffn = L.ffn, W = ffn >> 6;
+  const int s = blockIdx.x;
+  const int cb = s * sw, cw = min(sw, d - cb);
+  load_x_cols<NB, XT>(x, B, d, cb, cw, xs, sw);
+  if (words != nullptr) {
+    uint64_t* wl = reinterpret_cast<uint64_t*>(il + UPC_PMAX);  // [W]
+    int* pre = reinterpret_cast<int*>(wl + W);                  // [W + 1]
+    const int n = scan_words(words, W, wl, pre, red);
+    const int P = (n + gridDim.y - 1) / gridDim.y;
+    const int lo = blockIdx.y * P, hi = min(min(n, lo + P), lo + UPC_PMAX);
+    for (int w = threadIdx.x; w < W; w += BLOCK) {
+      int pos = pre[w];
+      if (pos >= hi || pre[w + 1] <= lo) continue;
+      uint64_t word = wl[w];
+      while (word) {
+        if (pos >= lo && pos < hi) il[pos - lo] = w * WAVE + __ffsll((unsigned long long)word) - 1;
+        ++pos;
+        word &= word - 1;
+      }
+    }
+    if (threadIdx.x == 0) s_cnt = max(0, hi - lo);
+  } else {
+    const int n = min(max(*n_in, 0), ffn);
+    const int P = (n + gridDim.y - 1) / gridDim.y;
+    const int lo = blockIdx.y * P, hi = min(min(n, lo + P), lo + UPC_PMAX);
+    int carry = 0;
+    for (int k0 = lo; k0 < hi; k0 += BLOCK) {
+      const int k = k0 + threadIdx.x;
+      const int i = (k < hi) ? idx_in[k] : -1;
+      const bool ok = (unsigned)i < (unsigned)ffn;
+      int total;
+      const int ex = block_exclusive_scan(ok ? 1 : 0, red, &total);
+      if (ok) il[carry + ex] = i;
+      carry += total;
+    }
+    if (threadIdx.x == 0) s_cnt = carry;
+  }
+  __syncthreads();
+  const int cnt = s_cnt;
+  const int lane = threadIdx.x % WAVE;
+  auto id_of = [il](int k) { return il[k]; };
+  auto stage = [](int, int) {};
+  auto out = [&](const int (&ids)[PW], int m, float (&acc)[ACT_RA][NB]) {
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      if (q >= m) break;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const float v = wave_sum(acc[NR * q + r][t]);
+          if (lane == t && t < B) hp[(((size_t)s * NR + r) * B + t) * ffn + ids[q]] = v;
+        }
+    }
+  };
+  act_rounds_cols<WT, ACT, NB, XT>(L, cnt, id_of, xs, sw, cb, cb + cw, cw, stage, out);
+}
+
+// a[t][i] = act(h + b_i) with h = the S slice partials of k_up_cols added in slice order
+// (ReGLU: max(h_gate + b_i, 0) * h_up), for the active neurons: the set bits of the union
+// words (thread k takes neuron k), or the index list (thread k takes entry k < n).
+template <int ACT>
+__global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, const float* __restrict__ hp,
+                                                   const uint64_t* __restrict__ words,
+                                                   const int32_t* __restrict__ idx_in,
+                                                   const int32_t* __restrict__ n_in, float* __restrict__ a) {
+  constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
+  const int ffn = L.ffn;
+  const int k = blockIdx.x * BLOCK + threadIdx.x;
+  int i;
+  if (words != nullptr) {
+    if (k >= ffn || !((words[k >> 6] >> (k & 63)) & 1ull)) return;
+    i = k;
+  } else {
+    if (k >= min(max(*n_in, 0), ffn)) return;
+    i = idx_in[k];
+    if ((unsigned)i >= (unsigned)ffn) return;
+  }
+  const float bias = L.b[i];
+  for (int t = 0; t < B; ++t) {
+    float h = 0.f, u = 0.f;
+    for (int s = 0; s < S; ++s) {
+      h += hp[(((size_t)s * NR) * B + t) * ffn + i];
+      if constexpr (NR == 2) u += hp[(((size_t)s * NR + 1) * B + t) * ffn + i];
+    }
+    float v;
+    if constexpr (ACT == ACT_REGLU) v = fmaxf(h + bias, 0.f) * u;
+    else v = act_one<ACT>(h + bias);
+    a[(size_t)t * ffn + i] = v;
   }
 }
 

@@ -30,6 +30,8 @@ struct pi_ctx {
   int32_t* idx = nullptr;       // [max_ffn]
   int32_t* nbuf = nullptr;      // [16]
   float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
+  float* hp = nullptr;          // slice partials of the column-sliced up GEMV
+  size_t hp_cap = 0;            // floats in hp
   float* part = nullptr;        // [32][max_batch][max_d] down-projection partial sums (groups or K splits)
   float* y = nullptr;           // [max_batch][max_d]
   uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
@@ -308,6 +310,80 @@ pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const in
   }
 }
 
+// Column-sliced up GEMV (k_up_cols + k_act_fin): for batches whose x is larger than
+// X_LDS_BUDGET, where the fused kernels would stage all of x in every workgroup with one
+// workgroup per CU. Slices are sw columns wide, a multiple of 512 whose x fits the budget.
+constexpr int UPC_WGS_PER_CU = 2;
+bool up_cols(int NB, int d, size_t xe) { return (size_t)NB * d * xe > X_LDS_BUDGET; }
+int up_cols_width(int NB, size_t xe) { return (int)(X_LDS_BUDGET / (NB * xe)) / 512 * 512; }
+size_t x_elem(const LayerDev& L) { return L.wtype == W_F32 ? 4 : 2; }
+bool use_up_cols(const LayerDev& L, int B) { return B <= 8 && up_cols(nb_for(B), L.d, x_elem(L)); }
+
+// Floats of hp for a context's limits: the largest slices x 2 rows x tokens x ffn over the
+// batch classes and element sizes that take the column-sliced path.
+size_t up_cols_floats(int max_batch, int max_d, int max_ffn) {
+  size_t m = 0;
+  for (int NB = 1; NB <= std::min(8, nb_for(std::min(max_batch, 8))); NB *= 2)
+    for (size_t xe : {(size_t)2, (size_t)4})
+      if (up_cols(NB, max_d, xe)) {
+        const int sw = up_cols_width(NB, xe);
+        m = std::max(m, (size_t)((max_d + sw - 1) / sw) * 2 * NB * max_ffn);
+      }
+  return m;
+}
+
+template <int WT, int ACT, int NB>
+pi_status launch_up_cols_t(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
+                           const int32_t* idx_in, const int32_t* n_in) {
+  typedef typename XType<WT == W_F32>::T XT;
+  const int sw = up_cols_width(NB, sizeof(XT));
+  const int S = (L.d + sw - 1) / sw;
+  constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
+  if ((size_t)S * NR * B * L.ffn > c->hp_cap)
+    return fail(c, PI_ERR_UNSUPPORTED, "layer %dx%d exceeds the context's slice buffer", L.d, L.ffn);
+  const int W = L.ffn / 64;
+  const size_t lds = (size_t)NB * sw * sizeof(XT) + UPC_PMAX * 4 + (words ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
+  if (lds + 256 > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the sliced up GEMV", L.ffn);
+  auto kern = k_up_cols<WT, ACT, NB>;
+  PI_HIP(c, allow_lds(kern, lds));
+  const int chunks = std::max((L.ffn + UPC_PMAX - 1) / UPC_PMAX, (UPC_WGS_PER_CU * c->cus + S - 1) / S);
+  PI_HIP(c, launch_k(c, K_UP, kern, dim3(S, chunks), lds, L, x, B, sw, words, idx_in, n_in, c->hp));
+  PI_HIP(c, launch_k(c, K_REDUCE, k_act_fin<ACT>, dim3((L.ffn + BLOCK - 1) / BLOCK), 0, L, B, S,
+                     (const float*)c->hp, words, idx_in, n_in, c->a));
+  return PI_OK;
+}
+
+template <int WT, int ACT>
+pi_status launch_up_cols_a(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
+                           const int32_t* idx_in, const int32_t* n_in) {
+  switch (nb_for(B)) {
+    case 1: return launch_up_cols_t<WT, ACT, 1>(c, L, x, B, words, idx_in, n_in);
+    case 2: return launch_up_cols_t<WT, ACT, 2>(c, L, x, B, words, idx_in, n_in);
+    case 4: return launch_up_cols_t<WT, ACT, 4>(c, L, x, B, words, idx_in, n_in);
+    default: return launch_up_cols_t<WT, ACT, 8>(c, L, x, B, words, idx_in, n_in);
+  }
+}
+
+template <int ACT>
+pi_status launch_up_cols_w(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
+                           const int32_t* idx_in, const int32_t* n_in) {
+  switch (L.wtype) {
+    case W_F32: return launch_up_cols_a<W_F32, ACT>(c, L, x, B, words, idx_in, n_in);
+    case W_F16: return launch_up_cols_a<W_F16, ACT>(c, L, x, B, words, idx_in, n_in);
+    default: return launch_up_cols_a<W_Q4, ACT>(c, L, x, B, words, idx_in, n_in);
+  }
+}
+
+// a of the active neurons from the union words (words != nullptr) or an index list.
+pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
+                         const int32_t* idx_in, const int32_t* n_in) {
+  switch (L.act) {
+    case ACT_RELU: return launch_up_cols_w<ACT_RELU>(c, L, x, B, words, idx_in, n_in);
+    case ACT_REGLU: return launch_up_cols_w<ACT_REGLU>(c, L, x, B, words, idx_in, n_in);
+    default: return launch_up_cols_w<ACT_SQRELU>(c, L, x, B, words, idx_in, n_in);
+  }
+}
+
 // Down projection over the active neurons (from the union words, SCAN, which also writes idx
 // and n; or from a given index list) into DOWN_G partial sums, then (y != nullptr) their sum
 // into y. With y == nullptr the partials stay in c->part for the next layer's glue.
@@ -541,7 +617,12 @@ pi_status enqueue_layer(pi_ctx* c, const pi_ffn* f, const XIn& xin, const void* 
   const LayerDev L = to_dev(f->desc);
   if (L.rank > 0) {
     PI_TRY(launch_stage1(c, L, xin, B));
-    PI_TRY(launch_stage2(c, L, B, mask, nullptr, x_cur));
+    if (use_up_cols(L, B)) {
+      PI_TRY(launch_stage2(c, L, B, mask, nullptr, nullptr));
+      PI_TRY(launch_up_cols(c, L, x_cur, B, c->munion, nullptr, nullptr));
+    } else {
+      PI_TRY(launch_stage2(c, L, B, mask, nullptr, x_cur));
+    }
   } else {
     PI_TRY(launch_truemask(c, L, xin, B, mask, nullptr, true));
   }
@@ -601,6 +682,8 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   const size_t o_idx = off; off += al(F * 4);
   const size_t o_n = off; off += al(16 * 4);
   const size_t o_a = off; off += al(B * F * 4);
+  const size_t hp_floats = up_cols_floats(max_batch, max_d, max_ffn);
+  const size_t o_hp = off; off += al(hp_floats * 4);
   const size_t o_part = off; off += al((size_t)std::max(DOWN_G_WIDE, MM_KSD) * B * D * 4);
   const size_t o_y = off; off += al(B * D * 4);
   const size_t o_x0 = off; off += al(B * D * 4);
@@ -631,6 +714,8 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   c->nbuf = reinterpret_cast<int32_t*>(c->ws + o_n);
   c->a = reinterpret_cast<float*>(c->ws + o_a);
   c->part = reinterpret_cast<float*>(c->ws + o_part);
+  c->hp = reinterpret_cast<float*>(c->ws + o_hp);
+  c->hp_cap = hp_floats;
   c->y = reinterpret_cast<float*>(c->ws + o_y);
   c->xbuf[0] = c->ws + o_x0;
   c->xbuf[1] = c->ws + o_x1;
@@ -754,7 +839,8 @@ pi_status pi_sparse_ffn(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B
   PI_HIP(ctx, hipSetDevice(ctx->device));
   const LayerDev L = to_dev(ffn->desc);
   if (B > 8) return batched_ffn(ctx, L, x, B, idx, n_active, y);
-  PI_TRY(launch_up(ctx, L, x, B, idx, n_active));
+  if (use_up_cols(L, B)) PI_TRY(launch_up_cols(ctx, L, x, B, nullptr, idx, n_active));
+  else PI_TRY(launch_up(ctx, L, x, B, idx, n_active));
   return launch_down<false>(ctx, L, B, idx, n_active, y, nullptr, nullptr, nullptr);
 }
 

@@ -148,6 +148,13 @@ def build_stack(cfg, seed, pi, ctx):
     return layers, ffns
 
 
+def up_cols(L, B):
+    """Whether the library runs the up GEMV over column slices of x (k_up_cols) for this layer
+    and batch: 1..8 tokens whose x, padded to the batch class 1/2/4/8, is above 64 KiB."""
+    nb = 1 if B <= 1 else 2 if B <= 2 else 4 if B <= 4 else 8
+    return B <= 8 and L.rank > 0 and nb * L.d * (4 if L.wtype == "f32" else 2) > 65536
+
+
 def kernel_bytes(cls, L, B, n_list):
     """Algorithmic bytes moved by the launches of one kernel class on one layer.
 
@@ -172,6 +179,8 @@ def kernel_bytes(cls, L, B, n_list):
     if cls == "stage1":
         return len(n_list) * (r * d * 2 + B * d * xe + B * r * 4)
     up_rows = lambda n: n * (k_up * d * w + 4 + 4 * B)  # noqa: E731  (rows, bias, a written)
+    if cls == "stage2" and up_cols(L, B):  # predictor stage 2 + threshold only
+        return len(n_list) * (F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8)
     if cls == "stage2":  # predictor stage 2 + threshold + own active neurons' up (gate) rows
         return sum(F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8 + B * d * xe + up_rows(n) for n in n_list)
     if cls == "truemask":  # threshold GEMV + (ReGLU) own active neurons' up rows
@@ -194,7 +203,7 @@ def step_bytes(layers, B, nlog_rows):
                 total += kernel_bytes("stage1", L, B, [n]) + kernel_bytes("stage2", L, B, [n])
             else:
                 total += kernel_bytes("truemask", L, B, [n])
-            if B > 8:
+            if B > 8 or up_cols(L, B):
                 total += kernel_bytes("up", L, B, [n])
             total += kernel_bytes("down", L, B, [n])
     return total
@@ -293,11 +302,11 @@ def main():
     npl = nprof.cpu().numpy()
     kb = {}
     for cls in ("stage1", "stage2", "truemask", "up", "down"):
-        if cls == "up" and B <= 8:
-            continue
         tot = 0.0
         for li, L in enumerate(layers):
             if (cls in ("stage1", "stage2") and L.rank == 0) or (cls == "truemask" and L.rank > 0):
+                continue
+            if cls == "up" and B <= 8 and not up_cols(L, B):
                 continue
             tot += kernel_bytes(cls, L, B, npl[:, li].tolist())
         kb[cls] = tot

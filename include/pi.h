@@ -20,9 +20,8 @@
  *  - Compute entry points allocate nothing: every scratch buffer (activations, partial
  *    sums, mask words, staging) belongs to the pi_ctx and is sized at pi_ctx_create.
  *  - No C++ exception crosses this boundary. A pi_ctx is used by one host thread at a time,
- *    and the work of one context must not run concurrently with itself (its scratch, and
- *    the arrival counts its down projection keeps at zero between calls, are shared): keep
- *    a context's calls on one stream, or order them.
+ *    and the work of one context must not run concurrently with itself (its scratch is
+ *    shared between calls): keep a context's calls on one stream, or order them.
  *  - Neuron index space: the "stored" order of the layer's rows. With a hot-first layout
  *    (pi_permute_rows), neuron_table[k] maps stored row k back to its original neuron.
  */
@@ -126,8 +125,8 @@ pi_status pi_predict(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, u
                      int32_t *idx, int32_t *n_active, float *logits_out);
 
 /* The neuron-aware sparse FFN on a given index list (P3 «Operator yang Sadar Neuron»): for
- * every listed neuron i, a_t,i = relu(w_up[i].x_t + b_i) (ReLU) or
- * relu(w_gate[i].x_t + b_i) * (w_up[i].x_t) (ReGLU), and y_t = sum_i a_t,i w_down_t[i].
+ * every listed neuron i, a_t,i = relu(w_up[i].x_t + b_i) (ReLU), its square (Squared-ReLU)
+ * or relu(w_gate[i].x_t + b_i) * (w_up[i].x_t) (ReGLU), and y_t = sum_i a_t,i w_down_t[i].
  * The one list applies to all B tokens.
  *   idx, n_active  device [ffn] int32 (each entry < ffn, no duplicates) and device int32
  *   y         [B][d] fp32 output (overwritten) */
@@ -163,10 +162,11 @@ pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, cons
 /* Kernel classes of pi_stack_profile's outputs, in this order:
  * predictor stage 1 (with the glue); predictor stage 2 + threshold + the activations of the
  * workgroup's active neurons; true-mask threshold GEMV + activations; gathered up/gate GEMV
- * (index-list entry point, and the matrix-core path's gathered GEMM); down projection (with
- * the index scan) into partial sums; the small kernels: sum of partial sums into y, glue
- * between layers of several tokens, compaction and predictor hi/lo split of the matrix-core
- * path. */
+ * (index-list entry point; the column-sliced GEMV that batches of 1..8 tokens whose x is
+ * above 64 KiB take instead of stage 2's activations; the matrix-core path's gathered GEMM);
+ * down projection (with the index scan) into partial sums; the small kernels: sum of
+ * partial sums into y, activations from the column slices' partial sums, glue between
+ * layers of several tokens, compaction and predictor hi/lo split of the matrix-core path. */
 #define PI_KERNEL_CLASSES 6
 
 /* pi_stack_run without a graph, every kernel dispatched with a pair of hipEvents

@@ -101,6 +101,11 @@ CASES = {
     "reglu-truemask-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 0, 8, 8),
     "f16-b8-xwindows": (_cfg("opt6.7b", d=12288, ffn=2048, rank=512), 0, 8, 8),
     "opt175-full-q4-b8": (_cfg("opt175b"), 0, 8, 8),
+    # x larger than 64 KiB: the up GEMV over column slices of x (last slice narrower)
+    "reglu-b8-cols": (_cfg("llama70b", d=8192, ffn=4096, rank=512), 0, 8, 8),
+    "sqrelu-q4-b4-cols": (_cfg("opt175b", act="sqrelu", d=16896, ffn=2048, rank=512), 0, 8, 4),
+    "f16-b3-cols-ragged": (_cfg("opt6.7b", d=8200, ffn=320, rank=136), 0, 6, 3),
+    "f16-b1-cols": (_cfg("opt6.7b", d=33280, ffn=512, rank=136), 0, 2, 1),
     # Squared-ReLU (one up row per neuron, a = max(h, 0)^2) on every path
     "sqrelu-small": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=4096, rank=512), 0, 8, 1),
     "sqrelu-full": (_cfg("opt6.7b", act="sqrelu"), 2, 2, 1),
@@ -211,6 +216,36 @@ def test_sparse_ffn_on_oracle_index_list():
     ref = oracle.sparse_ffn(H, xh, idx_h)
     for t in range(2):
         assert rel_l2(y[t].cpu().numpy(), ref[t]) <= TOL["f16"]
+
+
+@pytest.mark.parametrize("act", ["relu", "reglu"])
+def test_sparse_ffn_column_slices_on_oracle_index_list(act):
+    """pi_sparse_ffn at 8 tokens with fp32 weights and x above 64 KiB (column-sliced up
+    GEMV) on the oracle's union list with out-of-range entries mixed in (skipped), and on
+    an empty list (y = 0)."""
+    cfg = _cfg("tiny", act=act, d=2560, ffn=1024)
+    L = make_layer(cfg, 1, device="cuda")
+    H = L.to_host()
+    B = 8
+    x = make_tokens(cfg, B, device="cuda")
+    ctx = make_ctx([L])
+    ffn = pi.Ffn(ctx, L)
+    xh = x.cpu().numpy()
+    idx_h = oracle.compact(oracle.union(oracle.threshold(oracle.decision_values(H, xh))))
+    assert idx_h.size > 0
+    lst = np.insert(idx_h, [0, idx_h.size // 2, idx_h.size], [-1, cfg.ffn + 5, -7]).astype(np.int32)
+    idx = torch.from_numpy(np.concatenate([lst, np.zeros(cfg.ffn + 3 - lst.size, np.int32)])).cuda()
+    n = torch.tensor([lst.size], dtype=torch.int32, device="cuda")
+    y = torch.empty((B, cfg.d), dtype=torch.float32, device="cuda")
+    pi.sparse_ffn(ctx, ffn, x, idx, n, y)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_ffn(H, xh, idx_h)
+    for t in range(B):
+        assert rel_l2(y[t].cpu().numpy(), ref[t]) <= TOL["f32"]
+    n.zero_()
+    pi.sparse_ffn(ctx, ffn, x, idx, n, y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
 
 
 # ------------------------------------------------------------------------------- glue
