@@ -31,6 +31,7 @@ from .ffn import (  # noqa: F401
     hot_first_order,
     layer_forward,
     mask_words,
+    per_token_ffn,
     permute_layer,
     predictor_logits,
     rows_f64,

@@ -43,7 +43,9 @@ Readings taken where the pages are silent (each is a named choice):
   is the masked projection's bias.
 * ``v == theta`` (including -0.0) is inactive; NaN is inactive.
 * A batch uses the union of its tokens' masks for every token; ReLU zeroes
-  the neurons a token does not itself activate.
+  the neurons a token does not itself activate. Per-token masking (each token on
+  its own mask only, :func:`per_token_ffn`) is the alternative the library offers
+  as a mode; with the true mask the two agree.
 * ReGLU: only the gate has a bias; the mask is taken on the gate.
 * Squared-ReLU (named, not defined, by the pages): ``max(h, 0) ** 2`` of the up
   projection; like ReLU it has one row per neuron and the mask is taken on it.
@@ -185,6 +187,21 @@ def sparse_ffn(layer: dict, x: np.ndarray, idx: np.ndarray, chunk: int = 2048) -
         else:
             raise ValueError(layer["act"])
         y += a @ rows_f64(layer, "down_t", rows)
+    return y
+
+
+def per_token_ffn(layer: dict, x: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """Per-token masking of a batch: ``y[t] = sum over i with m[t, i] of a_{t,i} W_down[:, i]``.
+
+    Each token is processed on its own predicted neurons only, the operator of P3
+    «Operator yang Sadar Neuron» applied one token at a time with the mask P3
+    «Prediktor Kepadatan Adaptif» gives that token; the alternative to the union reading
+    for batches. Returns float64 ``[B][d]``."""
+    x = np.atleast_2d(np.asarray(x))
+    m = np.atleast_2d(np.asarray(m, dtype=bool))
+    y = np.zeros((x.shape[0], layer["d"]), dtype=np.float64)
+    for t in range(x.shape[0]):
+        y[t] = sparse_ffn(layer, x[t:t + 1], compact(m[t]))[0]
     return y
 
 

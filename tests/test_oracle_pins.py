@@ -75,6 +75,23 @@ def test_golden_reglu_tiny():
     np.testing.assert_array_equal(r["y"], g["y"])
 
 
+def test_golden_per_token_tiny():
+    """A predictor that misses a neuron one token activates: union and per-token differ by hand."""
+    g = _golden("per_token_tiny.json")
+    L = _layer_dict("relu", g["w_up"], g["b"], g["w_down_t"], rank=2,
+                    p_w1=np.array(g["p_w1"], dtype=np.float64), p_w2=np.array(g["p_w2"], dtype=np.float64),
+                    p_b=np.array(g["p_b"], dtype=np.float64))
+    x = np.array(g["x"], dtype=np.float64)
+    v = oracle.decision_values(L, x)
+    np.testing.assert_array_equal(v, g["v"])
+    m = oracle.threshold(v)
+    np.testing.assert_array_equal(m, g["mask"])
+    r = oracle.layer_forward(L, x)
+    np.testing.assert_array_equal(r["idx"], g["union_idx"])
+    np.testing.assert_array_equal(r["y"], g["y_union"])
+    np.testing.assert_array_equal(oracle.per_token_ffn(L, x, m), g["y_per_token"])
+
+
 def test_golden_predictor_tiny():
     g = _golden("predictor_tiny.json")
     w_up = np.zeros((4, 3))
@@ -282,6 +299,28 @@ def test_batch_union_equals_per_token_equals_dense():
             np.testing.assert_allclose(r["y"][t], dense(L, X[t]), atol=1e-12)
             own = oracle.layer_forward(L, X[t][None])
             np.testing.assert_allclose(r["y"][t], own["y"][0], atol=1e-12)
+
+
+def test_per_token_true_mask_equals_dense_and_single_token_equals_union():
+    """Per-token masking with the true mask gives each token its dense FFN (every activation
+    family); at one token it is the union path; with a random mask it is the per-token sum of
+    the chosen neurons' terms, one neuron at a time."""
+    rng = np.random.default_rng(21)
+    dense = {"relu": _dense_relu, "reglu": _dense_reglu, "sqrelu": _dense_sqrelu}
+    for act in ("relu", "reglu", "sqrelu"):
+        L = _random_layer(rng, act)
+        X = rng.normal(size=(6, 64))
+        m = oracle.threshold(oracle.true_preactivation(L, X))
+        y = oracle.per_token_ffn(L, X, m)
+        for t in range(6):
+            np.testing.assert_allclose(y[t], dense[act](L, X[t]), atol=1e-12)
+            one = oracle.layer_forward(L, X[t][None])
+            np.testing.assert_allclose(y[t], one["y"][0], atol=1e-12)
+        mr = rng.random((6, L["ffn"])) < 0.3
+        yr = oracle.per_token_ffn(L, X, mr)
+        for t in range(2):
+            terms = [oracle.sparse_ffn(L, X[t], np.array([i], dtype=np.int32))[0] for i in np.flatnonzero(mr[t])]
+            np.testing.assert_allclose(yr[t], np.sum(terms, axis=0), atol=1e-12)
 
 
 def test_q4_0_layer_sparse_equals_dense_on_dequantised_weights():
