@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import ACT, KERNEL_CLASSES, PI_OK, WTYPE, FfnDesc, PiError, _ptr, lib
+from ._lib import ACT, KERNEL_CLASSES, MASK_MODE, PI_OK, WTYPE, FfnDesc, PiError, _ptr, lib
 
 __all__ = ["Context", "Ffn", "PiError", "predict", "sparse_ffn", "layer", "compact", "glue", "stack_run",
            "stack_profile", "KERNEL_CLASSES",
@@ -35,6 +35,10 @@ class Context:
             raise PiError(st, "pi_ctx_create failed")
         self.handle = h
         self.max_batch, self.max_d, self.max_ffn, self.max_rank = max_batch, max_d, max_ffn, max_rank
+
+    def set_mask_mode(self, mode: str):
+        """Masking of batches: "union" (default) or "per_token" (pi_ctx_set_mask_mode)."""
+        self.check(lib().pi_ctx_set_mask_mode(self.handle, MASK_MODE[mode]))
 
     def check(self, status: int):
         if status != PI_OK:

@@ -16,6 +16,7 @@ PI_OK, PI_ERR_INVALID, PI_ERR_UNSUPPORTED, PI_ERR_OOM, PI_ERR_HIP = range(5)
 KERNEL_CLASSES = ("stage1", "stage2", "truemask", "up", "down", "reduce")
 ACT = {"relu": 0, "reglu": 1, "sqrelu": 2}
 WTYPE = {"f32": 0, "f16": 1, "q4_0": 2}
+MASK_MODE = {"union": 0, "per_token": 1}
 
 
 class FfnDesc(ctypes.Structure):
@@ -36,6 +37,7 @@ _SIGS = {
     "pi_ctx_create": (c_int32, [c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p)]),
     "pi_ctx_destroy": (None, [c_void_p]),
     "pi_ctx_set_stream": (c_int32, [c_void_p, c_void_p]),
+    "pi_ctx_set_mask_mode": (c_int32, [c_void_p, c_int32]),
     "pi_ffn_create": (c_int32, [c_void_p, POINTER(FfnDesc), POINTER(c_void_p)]),
     "pi_ffn_destroy": (None, [c_void_p]),
     "pi_predict": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),

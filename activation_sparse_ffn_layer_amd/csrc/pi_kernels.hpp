@@ -14,8 +14,9 @@
 //                                         takes one group of active neurons over one column
 //                                         slice into a partial sum; the partials are added
 //                                         in a fixed order by k_reduce or the next layer's glue
-// When x of the batch is above 64 KiB, stage 2 stops after the threshold and k_up_cols +
-// k_act_fin compute the activations over column slices of x instead.
+// Where the fused activations would make stage 2 slow (x of the batch above 64 KiB, Q4_0
+// rows, d >= 8192, 5..8 tokens), stage 2 stops after the threshold and k_up_cols (+ k_act_fin
+// when x is cut into several column slices) computes the activations instead.
 // Plus k_up (the index-list entry point's gathered GEMV), k_compact, k_threshold, k_glue,
 // k_reduce and k_permute_rows.
 //
@@ -873,13 +874,14 @@ __global__ __launch_bounds__(BLOCK) void k_up(LayerDev L, const void* __restrict
 }
 
 // ---------------------------------------------------------------------------------------
-// k_up_cols: the gathered up (and gate) GEMV over column slices of x, for batches whose x
-// would leave room for only one workgroup per CU in LDS (every workgroup of the fused
-// kernels stages all of it). Workgroup (s, c) stages the columns [s*sw, s*sw + sw) of x once
+// k_up_cols: the gathered up (and gate) GEMV as a kernel of its own, over column slices of
+// x when x would leave room for only one workgroup per CU in LDS (every workgroup of the
+// fused kernels stages all of it). Workgroup (s, c) stages the columns [s*sw, s*sw + sw) of x once
 // and takes the list positions [c*P, c*P + P), P = ceil(n / gridDim.y): for each of those
 // neurons i and tokens t, the slice's partial pre-activation row_i[slice] . x_t goes to
 // hp[s][r][t][i] (r = 0: the up row, or for ReGLU 0 = gate, 1 = up). k_act_fin adds the
-// slices in order and applies the activation. The list is the union words' set bits in
+// slices in order and applies the activation; with one slice (gridDim.x == 1) the kernel
+// writes a itself, with the same arithmetic. The list is the union words' set bits in
 // ascending order (words != nullptr) or the caller's index list (entries outside [0, ffn)
 // skipped). Each partial is computed as in the fused kernels: the lane sums of its chunks,
 // then the wave sum.
@@ -890,7 +892,8 @@ template <int WT, int ACT, int NB>
 __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __restrict__ x, int B, int sw,
                                                    const uint64_t* __restrict__ words,
                                                    const int32_t* __restrict__ idx_in,
-                                                   const int32_t* __restrict__ n_in, float* __restrict__ hp) {
+                                                   const int32_t* __restrict__ n_in, float* __restrict__ hp,
+                                                   float* __restrict__ a) {
   typedef typename XType<WT == W_F32>::T XT;
   constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
   constexpr int PW = ActPW<ACT>::PW;
@@ -941,7 +944,12 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
   const int lane = threadIdx.x % WAVE;
   auto id_of = [il](int k) { return il[k]; };
   auto stage = [](int, int) {};
+  const bool whole = gridDim.x == 1;
   auto out = [&](const int (&ids)[PW], int m, float (&acc)[ACT_RA][NB]) {
+    if (whole) {
+      act_store<ACT, NB>(L, B, lane, ids, m, acc, a);
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < PW; ++q) {
       if (q >= m) break;
@@ -1006,6 +1014,9 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
 //        the ascending index list idx and n.
 //  else: the given index list, filtered to the group's words in list order (an ascending
 //        list gives the same group lists, hence the same y, as SCAN).
+// tok_mask != nullptr (per-token masking, SCAN only): a[t][i] counts only where bit i of
+// token t's mask words tok_mask[t][ffn/64] is set; the scan keeps each listed neuron's token
+// bits next to it in LDS.
 // Q4_0 (QS lanes per 32-element block): QS = 1: a lane takes a whole block (16 code bytes);
 // QS = 4: a lane takes 4 code bytes, i.e. elements 4j..4j+3 and 16+4j..16+4j+3 of the block.
 // ---------------------------------------------------------------------------------------
@@ -1029,6 +1040,7 @@ template <int WT, int NB, bool SCAN, int U, int QS, int G>
 __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const uint64_t* __restrict__ words,
                                                      const int32_t* __restrict__ idx_in,
                                                      const int32_t* __restrict__ n_in, const float* __restrict__ a,
+                                                     const uint64_t* __restrict__ tok_mask,
                                                      float* __restrict__ part, int32_t* __restrict__ idx_out,
                                                      int32_t* __restrict__ n_out, int32_t* __restrict__ n_log) {
   static_assert(G >= 1 && (G & (G - 1)) == 0, "the group count is a power of two");
@@ -1042,6 +1054,8 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
   __shared__ int s_ng;
   const int d = L.d, ffn = L.ffn, W = ffn >> 6;
   int* il = reinterpret_cast<int*>(smem);  // the group's neurons [down_list_cap(W, G)]
+  // per-token masking: bit t of tb[j] = token t's mask bit of neuron il[j]
+  uint8_t* tb = reinterpret_cast<uint8_t*>(il + down_list_cap(W, G));
   if constexpr (SCAN) {
     if (blockIdx.x == gridDim.x - 1) {  // the compaction block: ascending idx and n
       uint64_t* wl = reinterpret_cast<uint64_t*>(smem);
@@ -1075,10 +1089,20 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
       const int q = q0 + threadIdx.x;
       const int w = g + G * q;
       uint64_t word = (q < nwg) ? words[w] : 0ull;
+      uint64_t tw[NB];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) tw[t] = (tok_mask != nullptr && q < nwg && t < B) ? tok_mask[(size_t)t * W + w] : 0ull;
       int total;
       int pos = carry + block_exclusive_scan(__popcll(word), red, &total);
       while (word) {
-        il[pos++] = w * WAVE + __ffsll((unsigned long long)word) - 1;
+        const int bit = __ffsll((unsigned long long)word) - 1;
+        if (tok_mask != nullptr) {
+          uint32_t bits = 0;
+#pragma unroll
+          for (int t = 0; t < NB; ++t) bits |= (uint32_t)((tw[t] >> bit) & 1ull) << t;
+          tb[pos] = (uint8_t)bits;
+        }
+        il[pos++] = w * WAVE + bit;
         word &= word - 1;
       }
       carry += total;
@@ -1112,17 +1136,23 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
   }
   for (int j0 = slot; j0 < ng; j0 += NSL * U) {
     int ii[U];
+    uint32_t tbits[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + NSL * u;
       ii[u] = (j < ng) ? il[j] : -1;
+      tbits[u] = (SCAN && tok_mask != nullptr && j < ng) ? tb[j] : 0xFFu;
     }
     // activations first (small, likely cached), then the rows
     float av[U][NB];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < NB; ++t) av[u][t] = (ii[u] >= 0 && t < B) ? a[(size_t)t * ffn + ii[u]] : 0.f;
+      for (int t = 0; t < NB; ++t) {
+        // per-token masking: token t takes neuron i only if its own mask has it
+        const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
+        av[u][t] = on ? a[(size_t)t * ffn + ii[u]] : 0.f;
+      }
     u32x4 w[U];
     float sc[U];
 #pragma unroll

@@ -31,6 +31,7 @@ struct pi_ctx {
   int32_t* nbuf = nullptr;      // [16]
   float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
   float* hp = nullptr;          // slice partials of the column-sliced up GEMV
+  int mask_mode = PI_MASK_UNION; // masking of batches (pi_ctx_set_mask_mode)
   size_t hp_cap = 0;            // floats in hp
   float* part = nullptr;        // [32][max_batch][max_d] down-projection partial sums (groups or K splits)
   float* y = nullptr;           // [max_batch][max_d]
@@ -310,14 +311,22 @@ pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const in
   }
 }
 
-// Column-sliced up GEMV (k_up_cols + k_act_fin): for batches whose x is larger than
-// X_LDS_BUDGET, where the fused kernels would stage all of x in every workgroup with one
-// workgroup per CU. Slices are sw columns wide, a multiple of 512 whose x fits the budget.
+// Separate up GEMV over column slices of x (k_up_cols, + k_act_fin for several slices)
+// instead of stage 2's fused activations. Always when x of the batch is larger than
+// X_LDS_BUDGET: the fused kernels would stage all of x in every workgroup, one workgroup per
+// CU. Also where the fused activations make stage 2's tail long: Q4_0 rows (dequantisation),
+// rows of 8192 or more columns, and 5..8 tokens. Measured on MI355X against the fused path
+// (tokens/s of the layer stacks): OPT-175B Q4_0 +10% at 1 token and +12% at 2; Falcon-40B
+// 0/+2/+4% at 1/2/4 tokens; Llama-2-70B +1/+2/+2%; OPT-6.7B (d = 4096) -10/-8/-5% at 1/2/4
+// tokens and +19% at 8. Slices are sw columns wide, a multiple of 512 whose x fits the budget.
 constexpr int UPC_WGS_PER_CU = 2;
 bool up_cols(int NB, int d, size_t xe) { return (size_t)NB * d * xe > X_LDS_BUDGET; }
 int up_cols_width(int NB, size_t xe) { return (int)(X_LDS_BUDGET / (NB * xe)) / 512 * 512; }
 size_t x_elem(const LayerDev& L) { return L.wtype == W_F32 ? 4 : 2; }
-bool use_up_cols(const LayerDev& L, int B) { return B <= 8 && up_cols(nb_for(B), L.d, x_elem(L)); }
+bool use_up_cols(const LayerDev& L, int B) {
+  const int NB = nb_for(B);
+  return B <= 8 && (up_cols(NB, L.d, x_elem(L)) || L.wtype == W_Q4 || L.d >= 8192 || NB >= 8);
+}
 
 // Floats of hp for a context's limits: the largest slices x 2 rows x tokens x ffn over the
 // batch classes and element sizes that take the column-sliced path.
@@ -339,17 +348,19 @@ pi_status launch_up_cols_t(pi_ctx* c, const LayerDev& L, const void* x, int B, c
   const int sw = up_cols_width(NB, sizeof(XT));
   const int S = (L.d + sw - 1) / sw;
   constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
-  if ((size_t)S * NR * B * L.ffn > c->hp_cap)
+  if (S > 1 && (size_t)S * NR * B * L.ffn > c->hp_cap)
     return fail(c, PI_ERR_UNSUPPORTED, "layer %dx%d exceeds the context's slice buffer", L.d, L.ffn);
   const int W = L.ffn / 64;
   const size_t lds = (size_t)NB * sw * sizeof(XT) + UPC_PMAX * 4 + (words ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
   if (lds + 256 > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the sliced up GEMV", L.ffn);
   auto kern = k_up_cols<WT, ACT, NB>;
   PI_HIP(c, allow_lds(kern, lds));
-  const int chunks = std::max((L.ffn + UPC_PMAX - 1) / UPC_PMAX, (UPC_WGS_PER_CU * c->cus + S - 1) / S);
-  PI_HIP(c, launch_k(c, K_UP, kern, dim3(S, chunks), lds, L, x, B, sw, words, idx_in, n_in, c->hp));
-  PI_HIP(c, launch_k(c, K_REDUCE, k_act_fin<ACT>, dim3((L.ffn + BLOCK - 1) / BLOCK), 0, L, B, S,
-                     (const float*)c->hp, words, idx_in, n_in, c->a));
+  // one round of workgroups: at most UPC_WGS_PER_CU per CU (their LDS allows no more)
+  const int chunks = std::max((L.ffn + UPC_PMAX - 1) / UPC_PMAX, std::max(1, UPC_WGS_PER_CU * c->cus / S));
+  PI_HIP(c, launch_k(c, K_UP, kern, dim3(S, chunks), lds, L, x, B, sw, words, idx_in, n_in, c->hp, c->a));
+  if (S > 1)
+    PI_HIP(c, launch_k(c, K_REDUCE, k_act_fin<ACT>, dim3((L.ffn + BLOCK - 1) / BLOCK), 0, L, B, S,
+                       (const float*)c->hp, words, idx_in, n_in, c->a));
   return PI_OK;
 }
 
@@ -395,12 +406,13 @@ constexpr int MM_KSD = 32;  // K splits of the batched down projection
 
 template <int WT, int NB, bool SCAN>
 pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
-                        int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+                        int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
   constexpr int QS = (WT == W_Q4 && NB > 2) ? 4 : 1;
   constexpr int U = (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
   const int W = L.ffn / 64;
   constexpr int G = down_groups(NB);
-  const size_t lds = std::max((size_t)down_list_cap(W, G) * 4, SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
+  // the group's list (+ its per-token bits), or the compaction block's words and prefix
+  const size_t lds = std::max((size_t)down_list_cap(W, G) * 5, SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
   constexpr size_t lds_static = (size_t)(BLOCK / DownGeom<WT, QS>::SEG) * (DownGeom<WT, QS>::SW + 1) * 4 + 256;
   if (lds + lds_static > c->lds_max)
     return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the down projection", L.ffn);
@@ -408,7 +420,7 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   PI_HIP(c, allow_lds(kern, lds));
   const int S = (L.d + DownGeom<WT, QS>::SW - 1) / DownGeom<WT, QS>::SW;
   // SCAN: one more block writes idx and n
-  PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a,
+  PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a, tok_mask,
                      c->part, idx_out, n_out, n_log));
   if (y != nullptr) {
     const int BD = B * L.d;
@@ -419,22 +431,22 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
 
 template <int WT, bool SCAN>
 pi_status launch_down_w(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
-                        int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+                        int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
   switch (nb_for(B)) {
-    case 1: return launch_down_t<WT, 1, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
-    case 2: return launch_down_t<WT, 2, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
-    case 4: return launch_down_t<WT, 4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
-    default: return launch_down_t<WT, 8, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    case 1: return launch_down_t<WT, 1, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+    case 2: return launch_down_t<WT, 2, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+    case 4: return launch_down_t<WT, 4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+    default: return launch_down_t<WT, 8, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
   }
 }
 
 template <bool SCAN>
 pi_status launch_down(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
-                      int32_t* idx_out, int32_t* n_out, int32_t* n_log) {
+                      int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
   switch (L.wtype) {
-    case W_F32: return launch_down_w<W_F32, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
-    case W_F16: return launch_down_w<W_F16, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
-    default: return launch_down_w<W_Q4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log);
+    case W_F32: return launch_down_w<W_F32, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+    case W_F16: return launch_down_w<W_F16, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+    default: return launch_down_w<W_Q4, SCAN>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
   }
 }
 
@@ -541,7 +553,7 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
 }
 
 pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int32_t* idx, const int32_t* n,
-                 float* y) {
+                 float* y, const uint32_t* tok_mask) {
   MmRows p{};
   p.x = x;
   p.B = B;
@@ -556,6 +568,7 @@ pi_status mm_ffn(pi_ctx* c, const LayerDev& L, const half_t* x, int B, const int
   p.a16 = c->a16;
   p.lda = c->lda;
   p.ffn = L.ffn;
+  p.tok_mask = tok_mask;
   switch (L.act) {
     case ACT_RELU: PI_TRY((launch_mm<EPI_ACT, ACT_RELU, false>(c, p, L.ffn, 1, K_UP))); break;
     case ACT_REGLU: PI_TRY((launch_mm<EPI_ACT, ACT_REGLU, false>(c, p, L.ffn, 1, K_UP))); break;
@@ -596,17 +609,19 @@ pi_status batched_predict(pi_ctx* c, const LayerDev& L, const void* x, int B, ui
 }
 
 pi_status batched_ffn(pi_ctx* c, const LayerDev& L, const void* x, int B, const int32_t* idx, const int32_t* n,
-                      float* y) {
+                      float* y, const uint32_t* tok_mask) {
   const half_t* xh = static_cast<const half_t*>(x);
-  return mm_ffn(c, L, xh, B, idx, n, y);
+  return mm_ffn(c, L, xh, B, idx, n, y, tok_mask);
 }
 
 pi_status enqueue_batched(pi_ctx* c, const pi_ffn* f, const void* x, int B, float* y, uint64_t* mask, int32_t* idx,
                           int32_t* n, int32_t* n_log) {
   const LayerDev L = to_dev(f->desc);
+  const bool per_tok = c->mask_mode == PI_MASK_PER_TOKEN;
+  if (per_tok && mask == nullptr) mask = c->mtok;
   PI_TRY(batched_predict(c, L, x, B, mask, nullptr));
   PI_TRY(launch_compact_log(c, L.ffn, idx, n, n_log));
-  return batched_ffn(c, L, x, B, idx, n, y);
+  return batched_ffn(c, L, x, B, idx, n, y, per_tok ? reinterpret_cast<const uint32_t*>(mask) : nullptr);
 }
 
 // Enqueue the whole layer for one batch: three kernels. xin: where x comes from; x_cur: the
@@ -615,6 +630,9 @@ pi_status enqueue_batched(pi_ctx* c, const pi_ffn* f, const void* x, int B, floa
 pi_status enqueue_layer(pi_ctx* c, const pi_ffn* f, const XIn& xin, const void* x_cur, int B, float* y,
                         uint64_t* mask, int32_t* idx, int32_t* n, int32_t* n_log) {
   const LayerDev L = to_dev(f->desc);
+  // per-token masking needs the tokens' masks: the context's when the caller takes none
+  const bool per_tok = c->mask_mode == PI_MASK_PER_TOKEN && B > 1;
+  if (per_tok && mask == nullptr) mask = c->mtok;
   if (L.rank > 0) {
     PI_TRY(launch_stage1(c, L, xin, B));
     if (use_up_cols(L, B)) {
@@ -626,7 +644,7 @@ pi_status enqueue_layer(pi_ctx* c, const pi_ffn* f, const XIn& xin, const void* 
   } else {
     PI_TRY(launch_truemask(c, L, xin, B, mask, nullptr, true));
   }
-  return launch_down<true>(c, L, B, nullptr, nullptr, y, idx, n, n_log);
+  return launch_down<true>(c, L, B, nullptr, nullptr, y, idx, n, n_log, per_tok ? mask : nullptr);
 }
 
 }  // namespace
@@ -758,6 +776,18 @@ pi_status pi_ctx_set_stream(pi_ctx* ctx, void* hip_stream) {
   return PI_OK;
 }
 
+pi_status pi_ctx_set_mask_mode(pi_ctx* ctx, int32_t mode) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (mode != PI_MASK_UNION && mode != PI_MASK_PER_TOKEN) return fail(ctx, PI_ERR_INVALID, "unknown mask mode %d", mode);
+  if (mode != ctx->mask_mode && ctx->gexec != nullptr) {  // a captured stack step has the old mode baked in
+    (void)hipGraphExecDestroy(ctx->gexec);
+    ctx->gexec = nullptr;
+    ctx->g_layers.clear();
+  }
+  ctx->mask_mode = mode;
+  return PI_OK;
+}
+
 pi_status pi_ffn_create(pi_ctx* ctx, const pi_ffn_desc* desc, pi_ffn** out) {
   if (ctx == nullptr || out == nullptr) return PI_ERR_INVALID;
   *out = nullptr;
@@ -838,10 +868,10 @@ pi_status pi_sparse_ffn(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B
   PI_TRY(check_dev_ptr(ctx, y, "y"));
   PI_HIP(ctx, hipSetDevice(ctx->device));
   const LayerDev L = to_dev(ffn->desc);
-  if (B > 8) return batched_ffn(ctx, L, x, B, idx, n_active, y);
+  if (B > 8) return batched_ffn(ctx, L, x, B, idx, n_active, y, nullptr);
   if (use_up_cols(L, B)) PI_TRY(launch_up_cols(ctx, L, x, B, nullptr, idx, n_active));
   else PI_TRY(launch_up(ctx, L, x, B, idx, n_active));
-  return launch_down<false>(ctx, L, B, idx, n_active, y, nullptr, nullptr, nullptr);
+  return launch_down<false>(ctx, L, B, idx, n_active, y, nullptr, nullptr, nullptr, nullptr);
 }
 
 pi_status pi_layer(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, float* y, uint64_t* mask, int32_t* idx,

@@ -45,9 +45,17 @@ struct MmRows {
   uint32_t* mask_union;  // EPI_MASK: [ffn/32]
   float* logits;         // EPI_MASK: [B][N] (nullable)
   half_t* a16;           // EPI_ACT: [Bp][lda] activations at compacted positions
+  const uint32_t* tok_mask;  // EPI_ACT: [B][ffn/32] mask words; token t keeps only its own
+                             // neurons (per-token masking). NULL: the union
   int lda;
   int ffn;
 };
+
+// Whether token t keeps neuron i: always under the union; its own mask bit under per-token
+// masking.
+__device__ __forceinline__ bool tok_keeps(const MmRows& p, int t, int i) {
+  return p.tok_mask == nullptr || ((p.tok_mask[(size_t)t * (p.ffn >> 5) + (i >> 5)] >> (i & 31)) & 1u);
+}
 
 // ---------------------------------------------------------------------------------------
 // k_mm_gemm: the row-tiled products C[t][n] = sum_k X[t][k] W[row(n)][k], tiled through LDS. A workgroup owns 64
@@ -177,21 +185,23 @@ __global__ __launch_bounds__(BLOCK) void k_mm_gemm(MmRows p) {
       }
       __syncthreads();
       if (rb == 0 && col < npad) {
-        const float bias = valid ? p.bias[p.idx != nullptr ? p.idx[col] : col] : 0.f;
+        const int nid = valid ? (p.idx != nullptr ? p.idx[col] : col) : 0;
+        const float bias = valid ? p.bias[nid] : 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * tb + mfma_row(r, lane);
           const float up = ex[(tb * 16 + r) * WAVE + lane];
-          const float a = (valid && t < p.B) ? fmaxf(acc[r] + bias, 0.f) * up : 0.f;
+          const float a = (valid && t < p.B && tok_keeps(p, t, nid)) ? fmaxf(acc[r] + bias, 0.f) * up : 0.f;
           if (t < p.B) p.a16[(size_t)t * p.lda + col] = (half_t)a;
         }
       }
     } else if (col < npad) {
-      const float bias = valid ? p.bias[p.idx != nullptr ? p.idx[col] : col] : 0.f;
+      const int nid = valid ? (p.idx != nullptr ? p.idx[col] : col) : 0;
+      const float bias = valid ? p.bias[nid] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * tb + mfma_row(r, lane);
-        const float a = (valid && t < p.B) ? act_one<ACT>(acc[r] + bias) : 0.f;
+        const float a = (valid && t < p.B && tok_keeps(p, t, nid)) ? act_one<ACT>(acc[r] + bias) : 0.f;
         if (t < p.B) p.a16[(size_t)t * p.lda + col] = (half_t)a;
       }
     }

@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the stack depth (exploration only)")
     ap.add_argument("--act", choices=["relu", "reglu", "sqrelu"], default=None,
                     help="override the workload's activation family (e.g. the Squared-ReLU variant)")
+    ap.add_argument("--mask", choices=["union", "per_token"], default="union",
+                    help="masking of a batch: the union of the tokens' masks, or each token's own")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-steps", type=int, default=16, help="steps of the per-kernel event pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -149,10 +151,12 @@ def build_stack(cfg, seed, pi, ctx):
 
 
 def up_cols(L, B):
-    """Whether the library runs the up GEMV over column slices of x (k_up_cols) for this layer
-    and batch: 1..8 tokens whose x, padded to the batch class 1/2/4/8, is above 64 KiB."""
+    """Whether the library runs the up GEMV as its own kernel (k_up_cols) rather than in stage 2
+    for this predictor layer and batch of 1..8 tokens: x (padded to the batch class 1/2/4/8)
+    above 64 KiB, Q4_0 rows, d >= 8192, or 5..8 tokens."""
     nb = 1 if B <= 1 else 2 if B <= 2 else 4 if B <= 4 else 8
-    return B <= 8 and L.rank > 0 and nb * L.d * (4 if L.wtype == "f32" else 2) > 65536
+    big_x = nb * L.d * (4 if L.wtype == "f32" else 2) > 65536
+    return B <= 8 and L.rank > 0 and (big_x or L.wtype == "q4_0" or L.d >= 8192 or nb >= 8)
 
 
 def kernel_bytes(cls, L, B, n_list):
@@ -209,10 +213,10 @@ def step_bytes(layers, B, nlog_rows):
     return total
 
 
-def cpu_baseline(cfg, layers, x_tokens, B, budget_s):
+def cpu_baseline(cfg, layers, x_tokens, B, budget_s, mask_mode="union"):
     """The fp64 oracle, as it stands, on a bounded sample: one batch of B tokens chained
-    through the stack (union semantics, like the GPU step) until the time budget runs out.
-    Layers are copied to the host one at a time as the oracle reaches them (not timed)."""
+    through the stack (union or per-token masking, like the GPU step) until the time budget
+    runs out. Layers are copied to the host one at a time as the oracle reaches them (not timed)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -226,7 +230,8 @@ def cpu_baseline(cfg, layers, x_tokens, B, budget_s):
         H = L.to_host()
         t0 = time.perf_counter()
         r = oracle.layer_forward(H, x)
-        x = oracle.glue(r["y"], x)
+        y = oracle.per_token_ffn(H, x, r["mask"]) if mask_mode == "per_token" else r["y"]
+        x = oracle.glue(y, x)
         elapsed += time.perf_counter() - t0
         done += 1
         del H
@@ -261,6 +266,7 @@ def main():
     stream = torch.cuda.current_stream()
     max_rank = max(cfg.layer_rank(0.2), 8)
     ctx = pi.Context(max_batch=B, max_d=cfg.d, max_ffn=cfg.ffn, max_rank=max_rank)
+    ctx.set_mask_mode(args.mask)
     log(f"generating {cfg.layers} layers of {cfg.name} on the GPU")
     t0 = time.perf_counter()
     layers, ffns = build_stack(cfg, args.seed, pi, ctx)
@@ -332,7 +338,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, layers, xt, B, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, layers, xt, B, args.cpu_seconds, args.mask)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -341,7 +347,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}-shaped {cfg.act} FFN stack, batch {B}", "layers": cfg.layers, "d": cfg.d,
                    "ffn": cfg.ffn, "rank": cfg.rank, "weights": cfg.wtype, "batch": B, "seed": args.seed,
-                   "hot_first": cfg.hot_first, "graph": use_graph},
+                   "hot_first": cfg.hot_first, "graph": use_graph, "mask": args.mask},
         "hbm_frac_active": round(frac_active, 4),
         "stream_read_gbs": round(stream_gbs, 1),
         "frac_of_stream_read": round(active_bytes / elapsed_s / 1e9 / stream_gbs, 4),

@@ -109,6 +109,22 @@ pi_status pi_ctx_set_stream(pi_ctx *ctx, void *hip_stream);
 pi_status pi_ffn_create(pi_ctx *ctx, const pi_ffn_desc *desc, pi_ffn **out);
 void pi_ffn_destroy(pi_ffn *ffn);
 
+/* Masking of a batch of B > 1 tokens in pi_layer, pi_stack_run and pi_stack_profile:
+ *  PI_MASK_UNION      (default) every token gets the activations of every neuron in the
+ *                     union of the batch's masks (ReLU zeroes the neurons it does not
+ *                     itself activate)
+ *  PI_MASK_PER_TOKEN  each token gets only its own predicted neurons, a_t,i = 0 where bit i
+ *                     of token t's mask is clear: the operator of P3 «Operator yang Sadar
+ *                     Neuron» applied one token at a time with the mask P3 «Prediktor
+ *                     Kepadatan Adaptif» gives that token.
+ * The same rows are read either way (those of the union). The mode is a property of the
+ * context; pi_sparse_ffn (one list for all tokens) does not depend on it. */
+typedef enum { PI_MASK_UNION = 0, PI_MASK_PER_TOKEN = 1 } pi_mask_mode;
+
+/* Set the context's masking of batches; PI_ERR_INVALID for another value. Work already
+ * enqueued keeps the mode it was enqueued with. */
+pi_status pi_ctx_set_mask_mode(pi_ctx *ctx, int32_t mode);
+
 /* Predict the active neurons of B tokens (P3 «Fase Online», «Prediktor Kepadatan Adaptif»).
  *   x         [B][d] fp16 (fp32 when wtype == PI_W_F32)
  *   mask      [B][ffn/64] uint64 per-token bits: bit j of word w is neuron 64w+j, set when
@@ -162,8 +178,9 @@ pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, cons
 /* Kernel classes of pi_stack_profile's outputs, in this order:
  * predictor stage 1 (with the glue); predictor stage 2 + threshold + the activations of the
  * workgroup's active neurons; true-mask threshold GEMV + activations; gathered up/gate GEMV
- * (index-list entry point; the column-sliced GEMV that batches of 1..8 tokens whose x is
- * above 64 KiB take instead of stage 2's activations; the matrix-core path's gathered GEMM);
+ * (index-list entry point; the separate, column-sliced GEMV that 1..8 tokens take instead
+ * of stage 2's activations when x is above 64 KiB, for Q4_0, d >= 8192 or 5..8 tokens; the
+ * matrix-core path's gathered GEMM);
  * down projection (with the index scan) into partial sums; the small kernels: sum of
  * partial sums into y, activations from the column slices' partial sums, glue between
  * layers of several tokens, compaction and predictor hi/lo split of the matrix-core path. */

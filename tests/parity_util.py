@@ -99,5 +99,36 @@ def check_layer(host: dict, x_host: np.ndarray, out: dict, tol: float, check_log
     return int(band.sum()), int(np.sum(diff))
 
 
+def check_layer_per_token(host: dict, x_host: np.ndarray, out: dict, tol: float):
+    """Parity of one batch under per-token masking: masks as in check_layer; y[t] is the
+    oracle's FFN of token t on its own mask, corrected for band neurons the HIP path decided
+    the other way for that token. Returns the number of such band decisions."""
+    ffn = host["ffn"]
+    v = oracle.decision_values(host, x_host)
+    m_or = oracle.threshold(v, host["threshold"])
+    band = oracle.band(v, host["threshold"])
+    m_gpu = words_to_bool(out["mask"], ffn)
+    B = x_host.shape[0]
+    diff = m_gpu != m_or
+    assert not np.any(diff & ~band), f"{int(np.sum(diff & ~band))} mask bits differ outside the band"
+    u_gpu = oracle.union(m_gpu)
+    n = int(out["n"].item())
+    assert n == int(u_gpu.sum())
+    np.testing.assert_array_equal(out["idx"][:n].cpu().numpy(), oracle.compact(u_gpu))
+    y_ref = oracle.per_token_ffn(host, x_host, m_or)
+    for t, i in zip(*np.nonzero(diff)):
+        c = oracle.sparse_ffn(host, x_host[t], np.array([i], dtype=np.int32))[0]
+        y_ref[t] = y_ref[t] + c if m_gpu[t, i] else y_ref[t] - c
+    y = out["y"].cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(y))
+    for t in range(B):
+        if np.all(y_ref[t] == 0.0):
+            assert np.all(y[t] == 0.0)
+        else:
+            e = rel_l2(y[t], y_ref[t])
+            assert e <= tol, f"token {t}: rel L2 {e:.3e} > {tol}"
+    return int(np.sum(diff))
+
+
 def layer_with(layer: Layer, **kw) -> Layer:
     return dataclasses.replace(layer, **kw)

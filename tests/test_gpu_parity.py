@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from synth import CONFIGS, make_decision_values, make_layer, make_tokens
-from tests.parity_util import TOL, check_layer, make_ctx, rel_l2, run_layer, words_to_bool
+from tests.parity_util import (TOL, check_layer, check_layer_per_token, make_ctx, rel_l2, run_layer,
+                               words_to_bool)
 
 pytestmark = pytest.mark.gpu
 
@@ -138,6 +139,72 @@ def test_layer_parity(case):
         bands += nb
         flips += nf
     _say(f"  {case}: band neurons {bands}, decided differently {flips}")
+
+
+# per-token masking: each token gets only its own predicted neurons (vector and matrix paths)
+PT_CASES = {
+    "pt-f16-b3": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 1, 6, 3),
+    "pt-sqrelu-b8": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=4096, rank=512), 1, 16, 8),
+    "pt-reglu-b8-cols": (_cfg("llama70b", d=8192, ffn=4096, rank=512), 0, 8, 8),
+    "pt-q4-b4": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 1, 8, 4),
+    "pt-truemask-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 0, 8, 8),
+    "pt-relu-b16-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 32, 16),
+    "pt-reglu-b64-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 2, 64, 64),
+}
+
+
+@pytest.mark.parametrize("case", list(PT_CASES))
+def test_layer_parity_per_token(case):
+    cfg, li, T, B = PT_CASES[case]
+    _say(f"per-token parity {case}: d={cfg.d} ffn={cfg.ffn} rank={cfg.rank} {cfg.wtype} {cfg.act} B={B}")
+    L = make_layer(cfg, li, device="cuda")
+    H = L.to_host()
+    X = make_tokens(cfg, T, device="cuda", stream=li + 2)
+    ctx = make_ctx([L], max_batch=max(8, B))
+    ffn = pi.Ffn(ctx, L)
+    flips = 0
+    differ = 0
+    for s in range(T // B):
+        x = X[s * B:(s + 1) * B].contiguous()
+        ctx.set_mask_mode("per_token")
+        out = run_layer(ctx, ffn, x)
+        flips += check_layer_per_token(H, x.cpu().numpy(), out, TOL[cfg.wtype])
+        ctx.set_mask_mode("union")
+        out_u = run_layer(ctx, ffn, x)
+        differ += int(torch.sum(torch.any(out_u["y"] != out["y"], dim=1)).item())
+    if cfg.rank is not None:
+        assert differ > 0, "per-token and union masking gave the same y for every token"
+    _say(f"  {case}: band decisions taken the other way {flips}; tokens whose y differs from the union's {differ}")
+
+
+def test_stack_per_token_mode_graph_and_switch():
+    """The mode reaches captured stack steps: per-token graph == per-token eager, a one-layer
+    stack equals pi_layer in that mode, and switching back to the union restores its result."""
+    cfg = _cfg("opt6.7b", layers=3, d=1024, ffn=4096, rank=512)
+    layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
+    X = make_tokens(cfg, 8, device="cuda")
+    ctx = make_ctx(layers, max_batch=4)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+
+    def run(graph, nl=3):
+        y = torch.empty((8, cfg.d), dtype=torch.float32, device="cuda")
+        pi.stack_run(ctx, ffns[:nl], X, 4, y, None, use_graph=graph)
+        return y
+
+    y_u = run(True)
+    ctx.set_mask_mode("per_token")
+    y_pg, y_pe = run(True), run(False)
+    y1 = run(True, nl=1)
+    ctx.set_mask_mode("union")
+    y_u2 = run(True)
+    ctx.set_mask_mode("per_token")
+    out = run_layer(ctx, ffns[0], X[:4].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y_pg, y_pe), "per-token graph and eager runs differ"
+    assert torch.equal(y_u, y_u2), "the union result changed after a mode round trip"
+    assert not torch.equal(y_u, y_pg), "the mode had no effect on the stack"
+    assert torch.equal(y1[:4], out["y"]), "one-layer stack and pi_layer differ in per-token mode"
+    check_layer_per_token(layers[0].to_host(), X[:4].cpu().numpy(), out, TOL["f16"])
 
 
 def test_empty_and_full_masks():
