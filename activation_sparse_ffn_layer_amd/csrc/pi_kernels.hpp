@@ -803,6 +803,36 @@ __device__ __forceinline__ int scan_words(const uint64_t* __restrict__ words, in
   return carry;
 }
 
+// The same scan with the first WPT * BLOCK words already loaded by the caller (wv[j] = word
+// threadIdx.x + BLOCK * j, 0 past W), so their latency can overlap other loads.
+template <int WPT>
+__device__ __forceinline__ int scan_words_pre(const uint64_t (&wv)[WPT], const uint64_t* __restrict__ words, int W,
+                                              uint64_t* wl, int* pre, int* red) {
+  int carry = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    if (j * BLOCK >= W) break;
+    const int w = j * BLOCK + threadIdx.x;
+    if (w < W) wl[w] = wv[j];
+    int total;
+    const int ex = block_exclusive_scan(__popcll(wv[j]), red, &total);
+    if (w < W) pre[w] = carry + ex;
+    carry += total;
+  }
+  for (int w0 = WPT * BLOCK; w0 < W; w0 += BLOCK) {
+    const int w = w0 + threadIdx.x;
+    const uint64_t word = (w < W) ? words[w] : 0ull;
+    if (w < W) wl[w] = word;
+    int total;
+    const int ex = block_exclusive_scan(__popcll(word), red, &total);
+    if (w < W) pre[w] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) pre[W] = carry;
+  __syncthreads();
+  return carry;
+}
+
 // ---------------------------------------------------------------------------------------
 // Compaction: ascending indices of the set bits of W union words. Workgroup g writes the
 // indices of words [256g, 256g+256): it counts all earlier set bits itself (no inter-
@@ -905,11 +935,19 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
   const int d = L.d, ffn = L.ffn, W = ffn >> 6;
   const int s = blockIdx.x;
   const int cb = s * sw, cw = min(sw, d - cb);
+  // the union words are loaded first, so their latency overlaps the staging of x
+  constexpr int WPT = 4;
+  uint64_t wv[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int w = j * BLOCK + threadIdx.x;
+    wv[j] = (words != nullptr && w < W) ? words[w] : 0ull;
+  }
   load_x_cols<NB, XT>(x, B, d, cb, cw, xs, sw);
   if (words != nullptr) {
     uint64_t* wl = reinterpret_cast<uint64_t*>(il + UPC_PMAX);  // [W]
     int* pre = reinterpret_cast<int*>(wl + W);                  // [W + 1]
-    const int n = scan_words(words, W, wl, pre, red);
+    const int n = scan_words_pre<WPT>(wv, words, W, wl, pre, red);
     const int P = (n + gridDim.y - 1) / gridDim.y;
     const int lo = blockIdx.y * P, hi = min(min(n, lo + P), lo + UPC_PMAX);
     for (int w = threadIdx.x; w < W; w += BLOCK) {
@@ -1050,7 +1088,6 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
   constexpr int NSL = BLOCK / SEG;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int red[NWAVES];
-  __shared__ float s_red[NSL][SW + 1];
   __shared__ int s_ng;
   const int d = L.d, ffn = L.ffn, W = ffn >> 6;
   int* il = reinterpret_cast<int*>(smem);  // the group's neurons [down_list_cap(W, G)]
@@ -1222,7 +1259,10 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[t][e] = fmaf(-8.f, qsum[t], acc[t][e]);
   }
-  // sum the NSL slots of each column (fixed order) and store this group's partial
+  // sum the NSL slots of each column (fixed order) and store this group's partial; the slots'
+  // sums [NSL][SW + 1] take the LDS of the neuron list, which no thread reads any more after
+  // the first barrier below
+  float (*s_red)[SW + 1] = reinterpret_cast<float (*)[SW + 1]>(smem);
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     if (t >= B) break;

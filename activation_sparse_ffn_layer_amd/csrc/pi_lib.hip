@@ -345,7 +345,8 @@ template <int WT, int ACT, int NB>
 pi_status launch_up_cols_t(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
                            const int32_t* idx_in, const int32_t* n_in) {
   typedef typename XType<WT == W_F32>::T XT;
-  const int sw = up_cols_width(NB, sizeof(XT));
+  // one slice when x fits: then only d (rounded up to 512) columns of LDS
+  const int sw = std::min(up_cols_width(NB, sizeof(XT)), (L.d + 511) / 512 * 512);
   const int S = (L.d + sw - 1) / sw;
   constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
   if (S > 1 && (size_t)S * NR * B * L.ffn > c->hp_cap)
@@ -411,9 +412,12 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   constexpr int U = (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
   const int W = L.ffn / 64;
   constexpr int G = down_groups(NB);
-  // the group's list (+ its per-token bits), or the compaction block's words and prefix
-  const size_t lds = std::max((size_t)down_list_cap(W, G) * 5, SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : 0);
-  constexpr size_t lds_static = (size_t)(BLOCK / DownGeom<WT, QS>::SEG) * (DownGeom<WT, QS>::SW + 1) * 4 + 256;
+  // the group's list (+ its per-token bits), then the slots' column sums; or the compaction
+  // block's words and prefix
+  constexpr size_t lds_red = (size_t)(BLOCK / DownGeom<WT, QS>::SEG) * (DownGeom<WT, QS>::SW + 1) * 4;
+  const size_t lds = std::max({(size_t)down_list_cap(W, G) * 5, lds_red,
+                               SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : (size_t)0});
+  constexpr size_t lds_static = 256;
   if (lds + lds_static > c->lds_max)
     return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the down projection", L.ffn);
   auto kern = k_down_part<WT, NB, SCAN, U, QS, G>;
