@@ -32,6 +32,7 @@ struct pi_ctx {
   float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
   float* hp = nullptr;          // slice partials of the column-sliced up GEMV
   int mask_mode = PI_MASK_UNION; // masking of batches (pi_ctx_set_mask_mode)
+  int down_g = 8;               // partial sums the last enqueued down projection left in part
   size_t hp_cap = 0;            // floats in hp
   float* part = nullptr;        // [32][max_batch][max_d] down-projection partial sums (groups or K splits)
   float* y = nullptr;           // [max_batch][max_d]
@@ -397,21 +398,22 @@ pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, con
 }
 
 // Down projection over the active neurons (from the union words, SCAN, which also writes idx
-// and n; or from a given index list) into DOWN_G partial sums, then (y != nullptr) their sum
-// into y. With y == nullptr the partials stay in c->part for the next layer's glue.
+// and n; or from a given index list) into G partial sums, then (y != nullptr) their sum into
+// y. With y == nullptr the partials stay in c->part for the next layer's glue, and c->down_g
+// says how many there are.
 constexpr int DOWN_G = 8;        // partial sums (groups) at 1..2 tokens
 constexpr int DOWN_G_WIDE = 16;  // at 3..8 tokens, whose union lists are longer
+constexpr int DOWN_G_LONG = 4;   // at 1..2 tokens with fp16/fp32 rows of 8192 or more columns
 constexpr int down_groups(int NB) { return NB >= 4 ? DOWN_G_WIDE : DOWN_G; }
 constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
 constexpr int MM_KSD = 32;  // K splits of the batched down projection
 
-template <int WT, int NB, bool SCAN>
-pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
+template <int WT, int NB, bool SCAN, int G>
+pi_status launch_down_g(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
                         int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
   constexpr int QS = (WT == W_Q4 && NB > 2) ? 4 : 1;
   constexpr int U = (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
   const int W = L.ffn / 64;
-  constexpr int G = down_groups(NB);
   // the group's list (+ its per-token bits), then the slots' column sums; or the compaction
   // block's words and prefix
   constexpr size_t lds_red = (size_t)(BLOCK / DownGeom<WT, QS>::SEG) * (DownGeom<WT, QS>::SW + 1) * 4;
@@ -426,11 +428,26 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   // SCAN: one more block writes idx and n
   PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a, tok_mask,
                      c->part, idx_out, n_out, n_log));
+  c->down_g = G;
   if (y != nullptr) {
     const int BD = B * L.d;
     PI_HIP(c, launch_k(c, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, c->part, G, BD, y));
   }
   return PI_OK;
+}
+
+// Groups: fewer, longer lists at 1..2 tokens when fp16/fp32 rows have 8192+ columns (the
+// glue then adds 4 partial sums). Measured on MI355X against 8 groups: Falcon-40B and
+// Llama-2-70B at one token +2.5% and +2.9% tokens/s (down 18.1 -> 16.7 us, 17.3 -> 16.2 us);
+// Q4_0 rows (OPT-175B) lose 7.5% with 4 groups, OPT-6.7B (d = 4096) is unchanged.
+template <int WT, int NB, bool SCAN>
+pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
+                        int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
+  if constexpr (WT != W_Q4 && NB <= 2) {
+    if (L.d >= 8192)
+      return launch_down_g<WT, NB, SCAN, DOWN_G_LONG>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+  }
+  return launch_down_g<WT, NB, SCAN, down_groups(NB)>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
 }
 
 template <int WT, bool SCAN>
@@ -1006,8 +1023,8 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
         // partials are added and the glue applied once, by two small kernels
         const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
         const int BD = B * d;
-        PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part,
-                             down_groups(nb_for(B)), BD, ctx->y));
+        PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part, ctx->down_g,
+                             BD, ctx->y));
         if (xe == 4)
           PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<true>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
         else
@@ -1017,7 +1034,7 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
       } else {
         const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
         // the glue adds the previous layer's partial sums itself
-        xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], DOWN_G, B * d};
+        xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], ctx->down_g, B * d};
         x_cur = ctx->xbuf[l & 1];
       }
       PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, l == L - 1 ? ctx->y : nullptr, nullptr, ctx->idx,

@@ -383,6 +383,33 @@ def test_stack_predictor_graph_equals_eager_and_is_deterministic():
     check_layer(H0, X[:2].cpu().numpy(), out, TOL["f16"])
 
 
+@pytest.mark.parametrize("d,B", [(8192, 1), (8192, 2), (4096, 1)])
+def test_stack_glue_of_partials_equals_layer_by_layer(d, B):
+    """The stack hands each layer's down partial sums (4 groups for fp16 rows of 8192+ columns
+    at 1..2 tokens, else 8) to the next layer's glue. Chaining pi_layer and pi_glue by hand,
+    which sums them first, gives the same y up to rounding."""
+    cfg = _cfg("falcon40b", layers=3, d=d, ffn=4096, rank=512)
+    layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
+    T = 2 * B
+    X = make_tokens(cfg, T, device="cuda", stream=5)
+    ctx = make_ctx(layers, max_batch=B)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+    y_stack = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    pi.stack_run(ctx, ffns, X, B, y_stack, None, use_graph=True)
+    for s in range(T // B):
+        x = X[s * B:(s + 1) * B].contiguous()
+        for li, f in enumerate(ffns):
+            out = run_layer(ctx, f, x)
+            if li + 1 < len(ffns):
+                xn = torch.empty_like(x)
+                pi.glue(ctx, out["y"], x, xn)
+                x = xn
+        torch.cuda.synchronize()
+        for t in range(B):
+            e = rel_l2(y_stack[s * B + t].cpu().numpy(), out["y"][t].cpu().numpy())
+            assert e <= TOL["f16"], f"step {s} token {t}: rel L2 {e:.3e}"
+
+
 # ------------------------------------------------------------------------ permutation
 
 def test_hot_first_permutation_on_device():
@@ -465,6 +492,8 @@ def test_stack_batched_graph_equals_eager():
 STACKS = {
     # name: (config, layers, tokens, batch)
     "opt6.7b-b1": (_cfg("opt6.7b", layers=3), 3, 2, 1),
+    "falcon40b-b1": (_cfg("falcon40b", layers=3), 3, 2, 1),   # 4 down partial sums into the glue
+    "llama70b-b2": (_cfg("llama70b", layers=2), 2, 4, 2),     # 4 partial sums through k_reduce
     "opt175b-q4-b8": (_cfg("opt175b", layers=2), 2, 8, 8),
     "llama70b-b64": (_cfg("llama70b", layers=2), 2, 64, 64),
 }
