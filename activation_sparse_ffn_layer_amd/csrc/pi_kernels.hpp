@@ -405,7 +405,7 @@ __device__ __forceinline__ void act_store(const LayerDev& L, int B, int lane, co
           const float u = wave_sum(acc[2 * q + 1][t]);
           v = fmaxf(g, 0.f) * u;
         }
-        if (lane == t && t < B) a[(size_t)t * L.ffn + ids[q]] = v;
+        if (lane == t && t < B) a[(size_t)ids[q] * NB + t] = v;
       }
     }
   }
@@ -610,7 +610,8 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
 // z = hi + lo (hi = fp16(z), lo = fp16(z - hi), together about 22 significant bits), so
 // W2 (fp16) . z runs on dot2 with exact products.
 // UP: then the workgroup's active neurons (up to 32) get their activations in balanced rounds
-// over its 4 waves; a is dense by neuron id ([B][ffn]). x is staged in LDS while the W2 rows
+// over its 4 waves; a is dense by neuron id with a neuron's NB tokens contiguous ([ffn][NB],
+// NB the batch class 1/2/4/8). x is staged in LDS while the W2 rows
 // are in flight (in column windows of width xw after the threshold when it does not fit).
 // ---------------------------------------------------------------------------------------
 template <int NB, int CPL, bool UP, int WT, int ACT>
@@ -753,7 +754,7 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
         if ((u >> lane) & 1ull)
 #pragma unroll
           for (int t = 0; t < NB; ++t)
-            if (t < B) a[(size_t)t * ffn + tile * WAVE + lane] = act_one_rt(L.act, vs[t][lane]);
+            if (t < B) a[(size_t)(tile * WAVE + lane) * NB + t] = act_one_rt(L.act, vs[t][lane]);
       }
     }
     if (lane == 0) s_union = u;
@@ -1024,6 +1025,7 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
     if ((unsigned)i >= (unsigned)ffn) return;
   }
   const float bias = L.b[i];
+  const int nb = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // a's token stride: the batch class
   for (int t = 0; t < B; ++t) {
     float h = 0.f, u = 0.f;
     for (int s = 0; s < S; ++s) {
@@ -1033,7 +1035,7 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
     float v;
     if constexpr (ACT == ACT_REGLU) v = fmaxf(h + bias, 0.f) * u;
     else v = act_one<ACT>(h + bias);
-    a[(size_t)t * ffn + i] = v;
+    a[(size_t)i * nb + t] = v;
   }
 }
 
@@ -1180,16 +1182,30 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
       ii[u] = (j < ng) ? il[j] : -1;
       tbits[u] = (SCAN && tok_mask != nullptr && j < ng) ? tb[j] : 0xFFu;
     }
-    // activations first (small, likely cached), then the rows
+    // activations first (small, likely cached; a neuron's NB tokens are contiguous), then the rows
     float av[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const float* ap = a + (size_t)(ii[u] >= 0 ? ii[u] : 0) * NB;
+      if constexpr (NB >= 4) {
+#pragma unroll
+        for (int t4 = 0; t4 < NB; t4 += 4) {
+          const u32x4 v4 = (ii[u] >= 0) ? ld16(ap + t4) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[u][t4 + e] = u2f(v4[e]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) av[u][t] = (ii[u] >= 0) ? ap[t] : 0.f;
+      }
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
-        // per-token masking: token t takes neuron i only if its own mask has it
+        // tokens past B hold no value; per-token masking: token t takes neuron i only if its
+        // own mask has it
         const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
-        av[u][t] = on ? a[(size_t)t * ffn + ii[u]] : 0.f;
+        av[u][t] = on ? av[u][t] : 0.f;
       }
+    }
     u32x4 w[U];
     float sc[U];
 #pragma unroll

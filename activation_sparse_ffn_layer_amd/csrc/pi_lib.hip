@@ -29,7 +29,7 @@ struct pi_ctx {
   uint64_t* munion = nullptr;   // [max_ffn/64]
   int32_t* idx = nullptr;       // [max_ffn]
   int32_t* nbuf = nullptr;      // [16]
-  float* a = nullptr;           // [max_batch][max_ffn], dense by neuron id
+  float* a = nullptr;           // [max_ffn][NB] on the vector path (NB = batch class 1/2/4/8), by neuron id
   float* hp = nullptr;          // slice partials of the column-sliced up GEMV
   int mask_mode = PI_MASK_UNION; // masking of batches (pi_ctx_set_mask_mode)
   int down_g = 8;               // partial sums the last enqueued down projection left in part
@@ -720,7 +720,7 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
   const size_t o_mu = off; off += al((F / 64) * 8);
   const size_t o_idx = off; off += al(F * 4);
   const size_t o_n = off; off += al(16 * 4);
-  const size_t o_a = off; off += al(B * F * 4);
+  const size_t o_a = off; off += al(std::max(B, (size_t)nb_for(std::min(max_batch, 8))) * F * 4);
   const size_t hp_floats = up_cols_floats(max_batch, max_d, max_ffn);
   const size_t o_hp = off; off += al(hp_floats * 4);
   const size_t o_part = off; off += al((size_t)std::max(DOWN_G_WIDE, MM_KSD) * B * D * 4);
