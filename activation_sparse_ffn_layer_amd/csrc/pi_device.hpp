@@ -21,6 +21,20 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Loads whose value is replaced by zeros where !ok. The load is always issued, so p must be
+// readable either way (callers clamp the index). Written as `ok ? load : 0`, the compiler
+// puts a branch around the load and copies its result register inside that branch, and the
+// copy waits for the load to arrive: loads meant to be in flight together then go out one
+// round trip at a time.
+__device__ __forceinline__ u32x4 ld16_or0(const void* p, bool ok) {
+  const u32x4 v = ld16(p);
+  return ok ? v : (u32x4){0, 0, 0, 0};
+}
+__device__ __forceinline__ u32x4 ld_stream_or0(const void* p, bool ok) {
+  const u32x4 v = ld_stream(p);
+  return ok ? v : (u32x4){0, 0, 0, 0};
+}
+
 // fp16 x fp16 pair dot product accumulated in fp32 (v_dot2c_f32_f16). Products of two fp16
 // values are exact in fp32.
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {

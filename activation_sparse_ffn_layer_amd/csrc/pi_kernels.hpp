@@ -93,7 +93,7 @@ template <> struct XType<true> { typedef float T; };
 
 // Per-token rms of y (0 for an all-zero y) into rms_s[NB].
 template <int NB>
-__device__ void glue_rms(const XIn& in, int B, int d, float* rms_s, float* red) {
+__device__ __forceinline__ void glue_rms(const XIn& in, int B, int d, float* rms_s, float* red) {
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     float ss = 0.f;
@@ -111,6 +111,9 @@ __device__ void glue_rms(const XIn& in, int B, int d, float* rms_s, float* red) 
   __syncthreads();
 }
 
+// The x-staging helpers are forced inline: a device function call starts with a wait for
+// every outstanding load, which would make the caller's weight loads issued before the glue
+// (k_stage1) complete before the glue issues its own.
 // Whole-width glue into LDS: xs[t][c] = round(y[t][c] / rms(y[t])) for c < d (x_prev[t][c]
 // when y[t] is all zero), rows t >= B zeroed; also stored to x_out when store_out. Every
 // 16-byte load of a token's y is issued before the first is used (d <= 4 * BLOCK * J;
@@ -118,7 +121,7 @@ __device__ void glue_rms(const XIn& in, int B, int d, float* rms_s, float* red) 
 constexpr int GLUE_J = 16;
 constexpr int GLUE_NY = 8;  // partial sums the whole-width glue takes (more go through y4_at)
 template <int NB, typename XT, int J = GLUE_J>
-__device__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red, bool store_out) {
+__device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red, bool store_out) {
   const int n4 = d >> 2;
   for (int t = 0; t < NB; ++t) {
     if (t >= B) {
@@ -130,7 +133,7 @@ __device__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red,
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int c = threadIdx.x + BLOCK * j;
-        v[j] = (c < n4) ? ld16(in.y + (size_t)t * d + 4 * c) : (u32x4){0, 0, 0, 0};
+        v[j] = ld16_or0(in.y + (size_t)t * d + 4 * min(c, n4 - 1), c < n4);
       }
     } else {
       // partial sums: four chunks at a time with all of their (up to GLUE_NY) partials in
@@ -144,8 +147,8 @@ __device__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red,
 #pragma unroll
             for (int g = 0; g < GLUE_NY; ++g) {
               const int c = threadIdx.x + BLOCK * (j0 + j);
-              p[j][g] = (c < n4 && g < in.ny) ? ld16(in.y + (size_t)g * in.ystride + (size_t)t * d + 4 * c)
-                                              : (u32x4){0, 0, 0, 0};
+              p[j][g] = ld16_or0(in.y + (size_t)min(g, in.ny - 1) * in.ystride + (size_t)t * d + 4 * min(c, n4 - 1),
+                                 c < n4 && g < in.ny);
             }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -190,7 +193,7 @@ __device__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red,
 
 // Stage x[:, c0 : c0+cw) of NB tokens into LDS xs[t][0..cw) (zeros for t >= B).
 template <int NB, bool XF32>
-__device__ void stage_x(const XIn& in, int B, int d, int c0, int cw, typename XType<XF32>::T* xs, int ldx,
+__device__ __forceinline__ void stage_x(const XIn& in, int B, int d, int c0, int cw, typename XType<XF32>::T* xs, int ldx,
                         const float* rms_s, bool store_out) {
   typedef typename XType<XF32>::T XT;
   for (int t = 0; t < NB; ++t) {
@@ -215,7 +218,7 @@ __device__ void stage_x(const XIn& in, int B, int d, int c0, int cw, typename XT
 // Copy x [NB][d] (fp16 or fp32 storage, rows t >= B zeroed) from global memory into LDS with
 // 16-byte accesses (d * sizeof(XT) is a multiple of 16).
 template <int NB, typename XT>
-__device__ void load_x(const void* x, int B, int d, XT* xs) {
+__device__ __forceinline__ void load_x(const void* x, int B, int d, XT* xs) {
   constexpr int E = 16 / sizeof(XT);
   const int n16 = d / E;
   for (int t = 0; t < NB; ++t)
@@ -247,7 +250,7 @@ __device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[RA], const 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = c0 + lane + WAVE * u;
-          w[q][u] = (c < nch) ? ld_stream(row[q] + (size_t)c * 16) : (u32x4){0, 0, 0, 0};
+          w[q][u] = ld_stream_or0(row[q] + (size_t)min(c, nch - 1) * 16, c < nch);
         }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -286,8 +289,10 @@ __device__ __forceinline__ void rows_dot(const uint8_t* const (&row)[RA], const 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = c0 + lane + WAVE * u;
-          w[q][u] = (c < nb) ? ld_stream(row[q] + (size_t)c * 16) : (u32x4){0, 0, 0, 0};
-          sc[q][u] = (c < nb) ? half_bits_to_float(srow[q][c]) : 0.f;
+          const int cc = min(c, nb - 1);
+          w[q][u] = ld_stream_or0(row[q] + (size_t)cc * 16, c < nb);
+          const float s = half_bits_to_float(srow[q][cc]);
+          sc[q][u] = (c < nb) ? s : 0.f;
         }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -413,7 +418,7 @@ __device__ __forceinline__ void act_store(const LayerDev& L, int B, int lane, co
 
 // Rounds over the columns [cb, ce) of the rows; out(ids, m, acc) takes each round's sums.
 template <int WT, int ACT, int NB, typename XT, typename IdOf, typename Stage, typename Out>
-__device__ void act_rounds_cols(const LayerDev& L, int cnt, IdOf id_of, const XT* xs, int ldx, int cb, int ce, int dw,
+__device__ __forceinline__ void act_rounds_cols(const LayerDev& L, int cnt, IdOf id_of, const XT* xs, int ldx, int cb, int ce, int dw,
                                 Stage stage, Out out) {
   constexpr int PW = ActPW<ACT>::PW;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
@@ -460,7 +465,7 @@ __device__ void act_rounds_cols(const LayerDev& L, int cnt, IdOf id_of, const XT
 }
 
 template <int WT, int ACT, int NB, typename XT, typename IdOf, typename Stage>
-__device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const XT* xs, int ldx, int dw, Stage stage,
+__device__ __forceinline__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const XT* xs, int ldx, int dw, Stage stage,
                            float* __restrict__ a) {
   const int lane = threadIdx.x % WAVE;
   auto out = [&](const int (&ids)[ActPW<ACT>::PW], int m, float (&acc)[ACT_RA][NB]) {
@@ -473,7 +478,7 @@ __device__ void act_rounds(const LayerDev& L, int B, int cnt, IdOf id_of, const 
 // 16-byte accesses (cw * sizeof(XT) % 16 == 0). The NB x cw/E chunks form one flat range:
 // each thread issues J loads (over all tokens) before storing any.
 template <int NB, typename XT>
-__device__ void load_x_cols(const void* x, int B, int d, int c0, int cw, XT* xs, int ldx) {
+__device__ __forceinline__ void load_x_cols(const void* x, int B, int d, int c0, int cw, XT* xs, int ldx) {
   constexpr int E = 16 / sizeof(XT);
   constexpr int J = 16;
   const int n16 = cw / E, total = NB * n16;
@@ -483,8 +488,8 @@ __device__ void load_x_cols(const void* x, int B, int d, int c0, int cw, XT* xs,
     for (int j = 0; j < J; ++j) {
       const int f = f0 + threadIdx.x + BLOCK * j;
       const int t = f / n16, c = f - t * n16;
-      v[j] = (f < total && t < B) ? ld16(reinterpret_cast<const XT*>(x) + (size_t)t * d + c0 + c * E)
-                                  : (u32x4){0, 0, 0, 0};
+      const bool ok = f < total && t < B;
+      v[j] = ld16_or0(reinterpret_cast<const XT*>(x) + (ok ? (size_t)t * d + c * E : 0) + c0, ok);
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -537,12 +542,12 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
   // and the staging of x, so their latency overlaps.
   constexpr int PF = 8;
   const int nch0 = min(dc, d) >> 3;
-  const uint8_t* wrow0 = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)row * d * 2;
+  const uint8_t* wrow0 = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
   u32x4 wp[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) {
     const int c = lane + WAVE * u;
-    wp[u] = (row < r && c < nch0) ? ld_stream(wrow0 + (size_t)c * 16) : (u32x4){0, 0, 0, 0};
+    wp[u] = ld_stream_or0(wrow0 + (size_t)min(c, nch0 - 1) * 16, row < r && c < nch0);
   }
   // x fits in LDS (and, for the glue, in one pass of registers): glue or copy it at once
   constexpr int GJ = (NB >= 8) ? 4 : (NB >= 4) ? 8 : GLUE_J;  // x of NB tokens in 64 KB: d <= 4 * BLOCK * GJ
@@ -635,7 +640,7 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + WAVE * j;
-      w[i][j] = (c < nch) ? ld_stream(w2 + ((size_t)(row0 + i) * r + c * 8) * 2) : (u32x4){0, 0, 0, 0};
+      w[i][j] = ld_stream_or0(w2 + ((size_t)(row0 + i) * r + min(c, nch - 1) * 8) * 2, c < nch);
     }
   uint32_t zh[NB][CPL][4], zl[NB][CPL][4];
 #pragma unroll
@@ -1173,6 +1178,11 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[t][e] = 0.f;
   }
+  // Rounds of U list items per slot, all their row pieces in flight. At 4..8 tokens a missing
+  // item (past the list's end) still issues its loads, from item 0's row, and drops them: with
+  // the loads under a branch the compiler waits for each one inside it (measured on MI355X:
+  // OPT-175B Q4_0 at 8 tokens, 77 -> 55 us per layer). At 1..2 tokens the branch is faster.
+  constexpr bool FULL = NB >= 4;
   for (int j0 = slot; j0 < ng; j0 += NSL * U) {
     int ii[U];
     uint32_t tbits[U];
@@ -1190,13 +1200,13 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
       if constexpr (NB >= 4) {
 #pragma unroll
         for (int t4 = 0; t4 < NB; t4 += 4) {
-          const u32x4 v4 = (ii[u] >= 0) ? ld16(ap + t4) : (u32x4){0, 0, 0, 0};
+          const u32x4 v4 = ld16(ap + t4);  // zeroed below where ii[u] < 0
 #pragma unroll
           for (int e = 0; e < 4; ++e) av[u][t4 + e] = u2f(v4[e]);
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < NB; ++t) av[u][t] = (ii[u] >= 0) ? ap[t] : 0.f;
+        for (int t = 0; t < NB; ++t) av[u][t] = ap[t];  // zeroed below where ii[u] < 0
       }
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
@@ -1212,14 +1222,22 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
     for (int u = 0; u < U; ++u) {
       w[u] = (u32x4){0, 0, 0, 0};
       sc[u] = 0.f;
-      if (ii[u] >= 0 && valid) {
-        if constexpr (WT == W_F16) w[u] = ld_stream(L.w_down_t + ((size_t)ii[u] * d + col0) * 2);
-        else if constexpr (WT == W_F32) w[u] = ld_stream(L.w_down_t + ((size_t)ii[u] * d + col0) * 4);
+      const bool ok = ii[u] >= 0 && valid;
+      if (FULL || ok) {
+        const size_t iu = (size_t)(ii[u] >= 0 ? ii[u] : ii[0]);
+        const int cv = valid ? col0 : 0;
+        if constexpr (WT == W_F16) w[u] = ld_stream_or0(L.w_down_t + (iu * d + cv) * 2, ok);
+        else if constexpr (WT == W_F32) w[u] = ld_stream_or0(L.w_down_t + (iu * d + cv) * 4, ok);
         else {
-          const size_t blk = (size_t)ii[u] * (d >> 5) + (col0 >> 5);
-          if constexpr (QS == 1) w[u] = ld_stream(L.w_down_t + blk * 16);
-          else w[u][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(L.w_down_t + blk * 16) + (sl & 3));
-          sc[u] = half_bits_to_float(L.s_down[blk]);
+          const size_t blk = iu * (d >> 5) + (cv >> 5);
+          if constexpr (QS == 1) {
+            w[u] = ld_stream_or0(L.w_down_t + blk * 16, ok);
+          } else {
+            const uint32_t q = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(L.w_down_t + blk * 16) + (sl & 3));
+            w[u] = (u32x4){ok ? q : 0u, 0u, 0u, 0u};
+          }
+          const float sv = half_bits_to_float(L.s_down[blk]);
+          sc[u] = ok ? sv : 0.f;
         }
       }
     }
