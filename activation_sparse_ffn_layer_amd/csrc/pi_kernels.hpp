@@ -176,16 +176,25 @@ __device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int 
     const float r = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
     const XT* xp = reinterpret_cast<const XT*>(in.x) + (size_t)t * d;
     XT* xo = reinterpret_cast<XT*>(in.x_out) + (size_t)t * d;
+    // r is the same in every thread: one branch, so the common case issues no load of x_prev
+    if (r != 0.f) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = threadIdx.x + BLOCK * j;
-      if (c < n4) {
+      for (int j = 0; j < J; ++j) {
+        const int c = threadIdx.x + BLOCK * j;
+        if (c < n4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const XT o = (r == 0.f) ? xp[4 * c + e] : (XT)(u2f(v[j][e]) / r);
-          xs[t * ldx + 4 * c + e] = o;
-          if (store_out) xo[4 * c + e] = o;
+          for (int e = 0; e < 4; ++e) {
+            const XT o = (XT)(u2f(v[j][e]) / r);
+            xs[t * ldx + 4 * c + e] = o;
+            if (store_out) xo[4 * c + e] = o;
+          }
         }
+      }
+    } else {
+      for (int c = threadIdx.x; c < d; c += BLOCK) {
+        const XT o = xp[c];
+        xs[t * ldx + c] = o;
+        if (store_out) xo[c] = o;
       }
     }
   }
