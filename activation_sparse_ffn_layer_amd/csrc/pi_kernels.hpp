@@ -120,8 +120,13 @@ __device__ __forceinline__ void glue_rms(const XIn& in, int B, int d, float* rms
 // d % 4 == 0). Same summation order as glue_rms.
 constexpr int GLUE_J = 16;
 constexpr int GLUE_NY = 8;  // partial sums the whole-width glue takes (more go through y4_at)
-template <int NB, typename XT, int J = GLUE_J>
-__device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red, bool store_out) {
+// after_issue() runs once, right after the first token's first y loads are issued: the
+// caller issues its own x-independent loads there, behind them, since loads complete in
+// issue order and the glue should not wait for the caller's.
+struct NoHook { __device__ void operator()() const {} };
+template <int NB, typename XT, int J = GLUE_J, typename Hook = NoHook>
+__device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red, bool store_out,
+                                       Hook after_issue = Hook()) {
   const int n4 = d >> 2;
   for (int t = 0; t < NB; ++t) {
     if (t >= B) {
@@ -135,6 +140,7 @@ __device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int 
         const int c = threadIdx.x + BLOCK * j;
         v[j] = ld16_or0(in.y + (size_t)t * d + 4 * min(c, n4 - 1), c < n4);
       }
+      if (t == 0) after_issue();
     } else {
       // partial sums: four chunks at a time with all of their (up to GLUE_NY) partials in
       // flight, added in partial order
@@ -150,6 +156,7 @@ __device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int 
               p[j][g] = ld16_or0(in.y + (size_t)min(g, in.ny - 1) * in.ystride + (size_t)t * d + 4 * min(c, n4 - 1),
                                  c < n4 && g < in.ny);
             }
+          if (t == 0 && j0 == 0) after_issue();
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             f32x4 acc = __builtin_bit_cast(f32x4, p[j][0]);
@@ -547,22 +554,26 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
   const int d = L.d, r = L.rank;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int row = blockIdx.x * NWAVES + wave;
-  // The weights do not depend on x: issue this wave's first 8 chunks per lane before the glue
-  // and the staging of x, so their latency overlaps.
+  // The weights do not depend on x: this wave's first 8 chunks per lane are issued before x
+  // is staged, so their latency overlaps. With the whole-width glue they go out right behind
+  // the glue's loads of y (loads complete in issue order, so the glue does not wait for them).
   constexpr int PF = 8;
   const int nch0 = min(dc, d) >> 3;
   const uint8_t* wrow0 = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
   u32x4 wp[PF];
+  auto issue_w1 = [&]() {
 #pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    const int c = lane + WAVE * u;
-    wp[u] = ld_stream_or0(wrow0 + (size_t)min(c, nch0 - 1) * 16, row < r && c < nch0);
-  }
+    for (int u = 0; u < PF; ++u) {
+      const int c = lane + WAVE * u;
+      wp[u] = ld_stream_or0(wrow0 + (size_t)min(c, nch0 - 1) * 16, row < r && c < nch0);
+    }
+  };
   // x fits in LDS (and, for the glue, in one pass of registers): glue or copy it at once
   constexpr int GJ = (NB >= 8) ? 4 : (NB >= 4) ? 8 : GLUE_J;  // x of NB tokens in 64 KB: d <= 4 * BLOCK * GJ
   const bool whole = dc >= d && (xin.y == nullptr || (d <= 4 * BLOCK * GJ && xin.ny <= GLUE_NY));
+  if (!(whole && xin.y != nullptr)) issue_w1();
   if (whole) {
-    if (xin.y != nullptr) glue_x<NB, half_t, GJ>(xin, B, d, xs, d, red, blockIdx.x == 0);
+    if (xin.y != nullptr) glue_x<NB, half_t, GJ>(xin, B, d, xs, d, red, blockIdx.x == 0, issue_w1);
     else load_x_cols<NB, half_t>(xin.x, B, d, 0, d, xs, d);
   } else if (xin.y != nullptr) {
     glue_rms<NB>(xin, B, d, rms_s, red);
@@ -1372,19 +1383,23 @@ __global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, con
   const float r = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
   const XT* xp = reinterpret_cast<const XT*>(x_prev) + (size_t)t * d;
   XT* xo = reinterpret_cast<XT*>(x_out) + (size_t)t * d;
+  if (r == 0.f) {  // all-zero y: x passes through (r is the same in every thread)
+    for (int c = threadIdx.x; c < d; c += BLOCK) xo[c] = xp[c];
+    return;
+  }
   for (int c0 = 0; c0 < n4; c0 += BLOCK * GLUE_J) {
     u32x4 v[GLUE_J];
 #pragma unroll
     for (int j = 0; j < GLUE_J; ++j) {
       const int c = c0 + threadIdx.x + BLOCK * j;
-      v[j] = (c < n4) ? ld16(yt + 4 * c) : (u32x4){0, 0, 0, 0};
+      v[j] = ld16_or0(yt + 4 * min(c, n4 - 1), c < n4);
     }
 #pragma unroll
     for (int j = 0; j < GLUE_J; ++j) {
       const int c = c0 + threadIdx.x + BLOCK * j;
       if (c < n4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xo[4 * c + e] = (r == 0.f) ? xp[4 * c + e] : (XT)(u2f(v[j][e]) / r);
+        for (int e = 0; e < 4; ++e) xo[4 * c + e] = (XT)(u2f(v[j][e]) / r);
     }
   }
 }
