@@ -662,27 +662,59 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
       const int c = lane + WAVE * j;
       w[i][j] = ld_stream_or0(w2 + ((size_t)(row0 + i) * r + min(c, nch - 1) * 8) * 2, c < nch);
     }
-  uint32_t zh[NB][CPL][4], zl[NB][CPL][4];
+  // z as fp16 pairs hi + lo. At 8 tokens without the fused activations they are staged once
+  // per workgroup in LDS ([NB][r/2] words each): in registers they took 128 VGPRs and left
+  // room for 2 waves per SIMD. Otherwise each lane keeps its own chunks in registers.
+  constexpr bool ZLDS = NB >= 8 && !UP;
+  constexpr int ZR = ZLDS ? 1 : NB;
+  uint32_t zh[ZR][CPL][4], zl[ZR][CPL][4];
+  uint32_t* zsh = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* zsl = zsh + NB * (r >> 1);
+  auto split = [](float f0, float f1, uint32_t& hi, uint32_t& lo) {
+    const half_t h0 = (half_t)f0, h1 = (half_t)f1;
+    const half_t l0 = (half_t)(f0 - (float)h0), l1 = (half_t)(f1 - (float)h1);
+    hi = __builtin_bit_cast(uint32_t, (half2_t){h0, h1});
+    lo = __builtin_bit_cast(uint32_t, (half2_t){l0, l1});
+  };
+  if constexpr (ZLDS) {
+    constexpr int ZJ = 8 * 1024 / 4 / BLOCK;  // float4 groups per thread at the largest rank
+    const int r4 = r >> 2, n4 = NB * r4;
+    u32x4 v[ZJ];
 #pragma unroll
-  for (int t = 0; t < NB; ++t)
+    for (int k = 0; k < ZJ; ++k) {
+      const int q = threadIdx.x + BLOCK * k;
+      const int t = q / r4, c4 = q - t * r4;
+      const bool ok = q < n4 && t < B;
+      v[k] = ld16_or0(z + (ok ? (size_t)t * r + 4 * c4 : 0), ok);
+    }
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + WAVE * j;
-      u32x4 a0 = (u32x4){0, 0, 0, 0}, a1 = (u32x4){0, 0, 0, 0};
-      if (t < B && c < nch) {
-        a0 = ld16(z + (size_t)t * r + c * 8);
-        a1 = ld16(z + (size_t)t * r + c * 8 + 4);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float f0 = u2f(e < 2 ? a0[2 * e] : a1[2 * e - 4]);
-        const float f1 = u2f(e < 2 ? a0[2 * e + 1] : a1[2 * e - 3]);
-        const half_t h0 = (half_t)f0, h1 = (half_t)f1;
-        const half_t l0 = (half_t)(f0 - (float)h0), l1 = (half_t)(f1 - (float)h1);
-        zh[t][j][e] = __builtin_bit_cast(uint32_t, (half2_t){h0, h1});
-        zl[t][j][e] = __builtin_bit_cast(uint32_t, (half2_t){l0, l1});
+    for (int k = 0; k < ZJ; ++k) {
+      const int q = threadIdx.x + BLOCK * k;
+      if (q < n4) {
+        const int t = q / r4, c4 = q - t * r4;
+        const int o = t * (r >> 1) + 2 * c4;
+        split(u2f(v[k][0]), u2f(v[k][1]), zsh[o], zsl[o]);
+        split(u2f(v[k][2]), u2f(v[k][3]), zsh[o + 1], zsl[o + 1]);
       }
     }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int t = 0; t < ZR; ++t)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + WAVE * j;
+        const bool ok = t < B && c < nch;
+        const float* zp = z + (ok ? (size_t)t * r + c * 8 : 0);
+        const u32x4 a0 = ld16_or0(zp, ok), a1 = ld16_or0(zp + 4, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f0 = u2f(e < 2 ? a0[2 * e] : a1[2 * e - 4]);
+          const float f1 = u2f(e < 2 ? a0[2 * e + 1] : a1[2 * e - 3]);
+          split(f0, f1, zh[t][j][e], zl[t][j][e]);
+        }
+      }
+  }
   if constexpr (UP) {
     if (xw >= L.d) load_x_cols<NB, XT>(x, B, L.d, 0, L.d, xs, L.d);
   }
@@ -692,6 +724,26 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
   uint8_t* mt = reinterpret_cast<uint8_t*>(mask_tok);
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
+    uint32_t hz[CPL][4], lz[CPL][4];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      if constexpr (ZLDS) {
+        const int o = t * (r >> 1) + min(lane + WAVE * j, nch - 1) * 4;  // w is 0 past nch
+        const u32x4 h4 = *reinterpret_cast<const u32x4*>(zsh + o);
+        const u32x4 l4 = *reinterpret_cast<const u32x4*>(zsl + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hz[j][e] = h4[e];
+          lz[j][e] = l4[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hz[j][e] = zh[t][j][e];
+          lz[j][e] = zl[t][j][e];
+        }
+      }
+    }
     float acc[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -700,8 +752,8 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
       for (int j = 0; j < CPL; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sum = dot2(w[i][j][e], zh[t][j][e], sum);
-          sum = dot2(w[i][j][e], zl[t][j][e], sum);
+          sum = dot2(w[i][j][e], hz[j][e], sum);
+          sum = dot2(w[i][j][e], lz[j][e], sum);
         }
       acc[i] = sum;
     }

@@ -196,7 +196,8 @@ template <int NB, int CPL, bool UP, int WT, int ACT>
 pi_status launch_stage2_t(pi_ctx* c, const LayerDev& L, int B, uint64_t* mtok, float* logits, const void* x) {
   const size_t xe = (WT == W_F32) ? 4 : 2;
   const int xw = UP ? x_window(c, NB, L.d, xe, c->lds_max) : L.d;
-  const size_t lds = UP ? (size_t)NB * xw * xe : 0;
+  // z in LDS at 8 tokens without the activations ([NB][rank] fp16 hi and lo)
+  const size_t lds = UP ? (size_t)NB * xw * xe : (NB >= 8 ? (size_t)NB * L.rank * 4 : 0);
   auto kern = k_stage2<NB, CPL, UP, WT, ACT>;
   PI_HIP(c, allow_lds(kern, lds));
   PI_HIP(c, launch_k(c, K_STAGE2, kern, dim3(L.ffn / STAGE2_TILE), lds, L, c->z, B, mtok, c->munion, logits, x, xw,
