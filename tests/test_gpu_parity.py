@@ -410,6 +410,31 @@ def test_stack_glue_of_partials_equals_layer_by_layer(d, B):
             assert e <= TOL["f16"], f"step {s} token {t}: rel L2 {e:.3e}"
 
 
+@pytest.mark.parametrize("B", [1, 2])
+def test_stack_glue_passes_x_through_an_all_zero_layer(B):
+    """A layer whose predictor marks no neuron gives y = 0, and the chaining then hands the
+    next layer the same x. At one token the next layer's stage 1 takes that branch in its own
+    glue, at two tokens the glue kernel does. Either way the second layer's y equals one
+    pi_layer call on the stack's input, bit for bit."""
+    cfg = _cfg("opt6.7b", layers=2, d=1024, ffn=2048, rank=512)
+    L0 = make_layer(cfg, 0, device="cuda")
+    L0 = dataclasses.replace(L0, b=torch.full_like(L0.b, -60.0), p_b=torch.full_like(L0.p_b, -60.0))
+    L1 = make_layer(cfg, 1, device="cuda")
+    T = 2 * B
+    X = make_tokens(cfg, T, device="cuda", stream=9)
+    ctx = make_ctx([L0, L1], max_batch=B)
+    ffns = [pi.Ffn(ctx, L0), pi.Ffn(ctx, L1)]
+    y_stack = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    nlog = torch.zeros((T // B, 2), dtype=torch.int32, device="cuda")
+    pi.stack_run(ctx, ffns, X, B, y_stack, nlog, use_graph=True)
+    torch.cuda.synchronize()
+    assert torch.all(nlog[:, 0] == 0) and torch.all(nlog[:, 1] > 0)
+    for s in range(T // B):
+        out = run_layer(ctx, ffns[1], X[s * B:(s + 1) * B].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(y_stack[s * B:(s + 1) * B], out["y"]), f"step {s}"
+
+
 # ------------------------------------------------------------------------ permutation
 
 def test_hot_first_permutation_on_device():
