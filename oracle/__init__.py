@@ -18,8 +18,13 @@ pages it restates. The pages are:
 Where a step is not fixed by the pages, the module docstring of
 :mod:`oracle.ffn` states the reading taken.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-and ``tests/test_synth_calibration.py``. None is "parity unpinned".
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_synth_calibration.py`` and ``tests/test_stack_chain.py``: hand-worked
+fixtures under ``tests/golden`` (``band`` by ``band.json``: exactly 1e-4 away is
+outside, 5e-5 off a nonzero theta inside, inf and NaN outside; ``stack_forward`` and
+``glue`` by ``stack_two_layers.json``: two layers, two tokens, the chaining vector,
+the all-zero pass-through and a predictor miss), the textbook dense FFN, brute-force
+loops, closed forms and invariants. None is "parity unpinned".
 """
 from .ffn import (  # noqa: F401
     THRESHOLD_BAND,

@@ -49,8 +49,14 @@ Readings taken where the pages are silent (each is a named choice):
 * ReGLU: only the gate has a bias; the mask is taken on the gate.
 * Squared-ReLU (named, not defined, by the pages): ``max(h, 0) ** 2`` of the up
   projection; like ReLU it has one row per neuron and the mask is taken on it.
-* Layers of a stack are chained by ``x_next = fp16(y / rms(y))`` (the pages
-  give no layer between FFNs); an all-zero y passes x through unchanged.
+* Layers of a stack are chained by ``x_next = fp16((y - c) / rms(y - c))`` (the
+  pages give no layer between FFNs), with ``c`` a fixed per-layer vector that
+  the input generator supplies: the expected y of the layer, so that the
+  tokens' common component is removed and each token's x keeps its own
+  direction through the stack. An all-zero y (or y == c) passes x through.
+* A hot prefix of H stored neurons (the hot neurons that PowerInfer keeps
+  resident and computes without asking the predictor) is always taken: their
+  decision value is +inf, and the activation itself zeroes the inactive ones.
 * Decision values within 1e-4 of theta form an exclusion band: there a
   float32 evaluation may legitimately decide either way.
 """
@@ -118,7 +124,20 @@ def true_preactivation(layer: dict, x: np.ndarray) -> np.ndarray:
 
 
 def decision_values(layer: dict, x: np.ndarray) -> np.ndarray:
-    return predictor_logits(layer, x) if layer["rank"] > 0 else true_preactivation(layer, x)
+    """Decision value of every neuron for each token x ``[B][d]``.
+
+    With a predictor, its logits; without, the true pre-activation. The first
+    ``layer["hot_prefix"]`` stored neurons (default 0) are computed for every
+    token without a prediction (P1 header bullets and «CPU/GPU hibrit çıkarım
+    yöntemi»: hot neurons are preloaded and always computed; P3 «Penempatan dan
+    Pengelolaan Neuron»): their value is +inf, so they are always above the
+    threshold and never inside the exclusion band."""
+    v = predictor_logits(layer, x) if layer["rank"] > 0 else true_preactivation(layer, x)
+    h = int(layer.get("hot_prefix", 0) or 0)
+    if h > 0:
+        v = np.array(v, dtype=np.float64, copy=True)
+        v[:, :h] = np.inf
+    return v
 
 
 def threshold(v: np.ndarray, theta: float = 0.0) -> np.ndarray:
@@ -127,8 +146,14 @@ def threshold(v: np.ndarray, theta: float = 0.0) -> np.ndarray:
 
 
 def band(v: np.ndarray, theta: float = 0.0) -> np.ndarray:
-    """Neurons whose decision value lies within ``THRESHOLD_BAND`` of theta."""
-    return np.abs(np.asarray(v, dtype=np.float64) - theta) < THRESHOLD_BAND
+    """Neurons whose decision value lies strictly within ``THRESHOLD_BAND`` of theta.
+
+    There the float32 evaluation of a kernel and this float64 one may legitimately
+    decide differently, so mask checks exclude these neurons and count them. The
+    distance is taken in float64; exactly 1e-4 away is outside the band; +-inf and
+    NaN are outside."""
+    with np.errstate(invalid="ignore"):
+        return np.abs(np.asarray(v, dtype=np.float64) - theta) < THRESHOLD_BAND
 
 
 def mask_words(m: np.ndarray) -> np.ndarray:
@@ -238,30 +263,35 @@ def permute_layer(layer: dict, perm: np.ndarray) -> dict:
     return out
 
 
-def glue(y: np.ndarray, x_prev: np.ndarray) -> np.ndarray:
-    """Next layer's input ``y / sqrt(mean(y^2))`` per token, rounded to x's storage type.
+def glue(y: np.ndarray, x_prev: np.ndarray, center=None) -> np.ndarray:
+    """Next layer's input per token: ``u = y - c``, ``x_next = u / sqrt(mean(u^2))``,
+    rounded to x's storage type (fp16 stacks to fp16, nearest even; fp32 stacks to fp32).
 
-    fp16 stacks round to fp16 (nearest even); fp32 stacks to fp32. An all-zero
-    y passes x_prev through unchanged."""
+    ``center`` is the layer's fixed vector c ``[d]`` (None: zero). A token whose y is all
+    zero (empty mask), or whose u is all zero, passes x_prev through unchanged."""
     y = np.atleast_2d(np.asarray(y, dtype=np.float64))
     x_prev = np.atleast_2d(np.asarray(x_prev))
+    c = np.zeros(y.shape[1]) if center is None else np.asarray(center, dtype=np.float64)
     out = np.empty(y.shape, dtype=x_prev.dtype)
     for t in range(y.shape[0]):
-        ss = float(np.sum(y[t] * y[t]))
-        if ss == 0.0:
+        u = y[t] - c
+        ss = float(np.sum(u * u))
+        if ss == 0.0 or not np.any(y[t] != 0.0):
             out[t] = x_prev[t]
         else:
-            out[t] = (y[t] / np.sqrt(ss / y.shape[1])).astype(x_prev.dtype)
+            out[t] = (u / np.sqrt(ss / y.shape[1])).astype(x_prev.dtype)
     return out
 
 
 def stack_forward(layers, x0: np.ndarray):
-    """Run a stack one batch at a time, chaining layers by :func:`glue`. Returns per-layer results."""
+    """Run a stack one batch at a time (P3 intro: each token passes through the whole
+    model before the next), chaining layer l to l + 1 by :func:`glue` with layer l's
+    ``glue_center``. Returns per-layer results, each with the layer's input ``x``."""
     x = np.atleast_2d(np.asarray(x0))
     results = []
     for layer in layers:
         r = layer_forward(layer, x)
         r["x"] = x
         results.append(r)
-        x = glue(r["y"], x)
+        x = glue(r["y"], x, layer.get("glue_center"))
     return results

@@ -36,6 +36,21 @@ Recipe (one layer of one workload):
   (``w_down_t[i]`` is neuron i's output column).
 * Q4_0 storage: see :func:`quantize_q4_0`.
 * Tokens: x ~ N(0, 1), stored fp16 (fp32 for fp32 workloads).
+* Chaining vector of a stack: ``glue_center = sum_i E[a_i] * w_down_t[i]`` (fp32 [d], from
+  the drawn down weights before storage rounding), the layer's expected output. It is
+  subtracted before the next layer's normalisation, which removes the component that every
+  token's y shares, so that deep ReLU stacks keep their tokens' inputs independent.
+  E[a_i] is taken for x ~ N(0, I): the pre-activation is ``h ~ N(b_i, sh_i^2)`` and the
+  predictor logit ``h + n`` with independent ``n ~ N(0, sn_i^2)``, where by the construction
+  above ``sh_i^2 = |p_i|^2 / (1 + s2)`` and ``sn_i^2 = |p_i|^2 s2 / (1 + s2)`` (without a
+  predictor, ``sh_i`` is the drawn row's norm and the mask is h > 0). A token's activation
+  counts where its own logit is positive, and in a batch of B tokens under the union also
+  where another token's is (probability ``1 - (1 - q_i)^(B-1)``, ``q_i = P(h + n > 0)``):
+  ``E[a] = E[f(h) P(n > -h)] + E[f(h) P(n <= -h)] (1 - (1 - q)^(B-1))`` with f the ReLU or
+  its square, by quadrature over h. ReGLU layers have none (their gate and up rows are drawn
+  independently, so the expected activation is zero). The vector therefore depends on the
+  batch size and masking the stack is run with (``make_layer``'s ``chain_batch`` and
+  ``chain_mode``).
 """
 from __future__ import annotations
 
@@ -121,6 +136,36 @@ def expected_top_share(p: np.ndarray, top_fraction: float) -> float:
     return float(mass[:k].sum() / mass.sum())
 
 
+def chain_activation(b: np.ndarray, sh: np.ndarray, sn: Optional[np.ndarray], act: str, batch: int,
+                     mode: str = "union", points: int = 801) -> np.ndarray:
+    """E[a_i] of each neuron for x ~ N(0, I) (input-side calibration of the chaining vector).
+
+    ``h ~ N(b, sh^2)``; ``sn`` the predictor noise std (None: no predictor, mask h > 0).
+    Under the union of a batch of ``batch`` tokens a neuron a token does not predict itself
+    still counts when another token predicts it. Quadrature over h on +-8 sh."""
+    if act == "reglu":
+        return np.zeros_like(b, dtype=np.float64)
+    g = np.linspace(-8.0, 8.0, points)
+    wq = np.exp(-0.5 * g * g) / math.sqrt(2.0 * math.pi) * (g[1] - g[0])
+    b = np.asarray(b, dtype=np.float64)[:, None]
+    sh = np.asarray(sh, dtype=np.float64)[:, None]
+    h = b + sh * g[None, :]
+    f = np.maximum(h, 0.0)
+    if act == "sqrelu":
+        f = f * f
+    elif act != "relu":
+        raise ValueError(act)
+    if sn is None:
+        return (f * wq).sum(axis=1)
+    pv = sp.ndtr(h / np.asarray(sn, dtype=np.float64)[:, None])     # P(logit > 0 | h)
+    own = (f * pv * wq).sum(axis=1)
+    if mode == "per_token" or batch <= 1:
+        return own
+    other = (f * (1.0 - pv) * wq).sum(axis=1)
+    q = (pv * wq).sum(axis=1)
+    return own + other * (1.0 - (1.0 - q) ** (batch - 1))
+
+
 @functools.lru_cache(maxsize=None)
 def solve_alpha(top_fraction: float, share: float, ffn: int, mean: float) -> float:
     """Power-law exponent at which the top ``top_fraction`` of neurons carry ``share`` of the mass."""
@@ -139,7 +184,7 @@ def solve_alpha(top_fraction: float, share: float, ffn: int, mean: float) -> flo
 # Q4_0 storage
 # --------------------------------------------------------------------------------------------
 
-def quantize_q4_0(w: torch.Tensor, chunk_rows: int = 2048):
+def quantize_q4_0(w: torch.Tensor, chunk_rows: int = 2048, values: bool = False):
     """Quantise rows of ``w`` [rows][d] (d % 32 == 0) to Q4_0 storage.
 
     Per block of 32 consecutive elements of a row: scale ``s = fp16(absmax / 8)``
@@ -149,6 +194,11 @@ def quantize_q4_0(w: torch.Tensor, chunk_rows: int = 2048):
     codes ``uint8 [rows][d/32][16]`` where byte j of a block holds element j in
     its low nibble and element j + 16 in its high nibble, and scales
     ``float16 [rows][d/32]``. The stored value of an element is (q - 8) * s.
+
+    With ``values`` also returns, as fp32 ``[rows][d]``, the value each code was chosen
+    to stand for, (q - 8) * s, taken from the quantiser's own rounding (before the codes
+    are packed). The generator uses it only to calibrate the chaining vector; the kernels
+    and the oracle decode the packed codes themselves.
     """
     rows, d = w.shape
     if d % 32:
@@ -156,6 +206,7 @@ def quantize_q4_0(w: torch.Tensor, chunk_rows: int = 2048):
     nb = d // 32
     codes = torch.empty((rows, nb, 16), dtype=torch.uint8, device=w.device)
     scales = torch.empty((rows, nb), dtype=torch.float16, device=w.device)
+    vals = torch.empty((rows, d), dtype=torch.float32, device=w.device) if values else None
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
         blk = w[r0:r1].reshape(r1 - r0, nb, 32).to(torch.float64)
@@ -163,9 +214,14 @@ def quantize_q4_0(w: torch.Tensor, chunk_rows: int = 2048):
         s64 = s16.to(torch.float64).unsqueeze(-1)
         safe = torch.where(s64 > 0, s64, torch.ones_like(s64))
         q = torch.where(s64 > 0, torch.round(blk / safe) + 8.0, torch.full_like(blk, 8.0))
-        q = q.clamp_(0.0, 15.0).to(torch.uint8)
+        q = q.clamp_(0.0, 15.0)
+        if values:
+            vals[r0:r1] = ((q - 8.0) * s64).reshape(r1 - r0, d).to(torch.float32)
+        q = q.to(torch.uint8)
         codes[r0:r1] = q[..., :16] | (q[..., 16:] << 4)
         scales[r0:r1] = s16
+    if values:
+        return codes, scales, vals
     return codes, scales
 
 
@@ -200,16 +256,18 @@ class Layer:
     p: np.ndarray          # activation probability profile (host)
     mean: float
     alpha: float
+    glue_center: Optional[torch.Tensor] = None   # fp32 [d] chaining vector, None for ReGLU
+    hot_prefix: int = 0    # stored neurons [0, hot_prefix) taken without a prediction
 
     def tensors(self):
         return {k: getattr(self, k) for k in ("w_up", "w_gate", "w_down_t", "s_up", "s_gate", "s_down",
-                                              "b", "p_w1", "p_w2", "p_b")}
+                                              "b", "p_w1", "p_w2", "p_b", "glue_center")}
 
     def to_host(self) -> dict:
         """Plain numpy copy of every stored array plus the scalar fields."""
         out = {k: (None if v is None else v.detach().cpu().numpy()) for k, v in self.tensors().items()}
         out.update(d=self.d, ffn=self.ffn, rank=self.rank, act=self.act, wtype=self.wtype,
-                   threshold=self.threshold)
+                   threshold=self.threshold, hot_prefix=self.hot_prefix)
         return out
 
     def nbytes(self) -> int:
@@ -229,7 +287,10 @@ def layer_mean(cfg: StackConfig, layer: int, master: int = 0) -> float:
     return float(np_rng(master, cfg.index, layer, _T_MEAN).uniform(lo, hi))
 
 
-def make_layer(cfg: StackConfig, layer: int, master: int = 0, device="cpu") -> Layer:
+def make_layer(cfg: StackConfig, layer: int, master: int = 0, device="cpu", chain_batch: int = 1,
+               chain_mode: str = "union") -> Layer:
+    """One seeded layer of ``cfg``. ``chain_batch`` / ``chain_mode``: the batch size and masking
+    (union or per_token) the stack will run with, which its chaining vector is computed for."""
     d, ffn = cfg.d, cfg.ffn
     mean = layer_mean(cfg, layer, master)
     if cfg.alpha is not None:
@@ -264,24 +325,48 @@ def make_layer(cfg: StackConfig, layer: int, master: int = 0, device="cpu") -> L
         w_mask = _randn((ffn, d), sd, s(_T_UP), device)
     w_down = _randn((ffn, d), sd, s(_T_DOWN), device)
     w_plain = _randn((ffn, d), sd, s(_T_PLAIN), device) if cfg.act == "reglu" else None
+    chain = cfg.act != "reglu"
 
-    def store(w):
+    def store(w, values=False):
+        """Stored form (weights, Q4_0 scales) and, with ``values``, what it stands for in fp32."""
         if w is None:
-            return None, None
+            return None, None, None
         if cfg.wtype == "f32":
-            return w, None
+            return w, None, (w if values else None)
         if cfg.wtype == "f16":
-            return w.to(torch.float16), None
+            h = w.to(torch.float16)
+            return h, None, (h.to(torch.float32) if values else None)
         if cfg.wtype == "q4_0":
-            return quantize_q4_0(w)
+            if values:
+                return quantize_q4_0(w, values=True)
+            return (*quantize_q4_0(w), None)
         raise ValueError(cfg.wtype)
 
-    m_w, m_s = store(w_mask)
+    m_w, m_s, m_val = store(w_mask, chain)
     del w_mask
-    dn_w, dn_s = store(w_down)
+    dn_w, dn_s, dn_val = store(w_down, chain)
     del w_down
-    pl_w, pl_s = store(w_plain)
+    pl_w, pl_s, _ = store(w_plain)
     del w_plain
+    glue_center = None
+    if chain:
+        # spreads of the stored masked rows' pre-activation and of the predictor's noise
+        sig_h = torch.sqrt((m_val * m_val).sum(dim=1)).double().cpu().numpy()
+        sig_n = None
+        if r > 0:
+            w1f = p_w1.to(torch.float32)
+            sn = torch.empty(ffn, dtype=torch.float32, device=device)
+            for r0 in range(0, ffn, 4096):
+                nr = p_w2[r0:r0 + 4096].to(torch.float32) @ w1f - m_val[r0:r0 + 4096]
+                sn[r0:r0 + 4096] = torch.sqrt((nr * nr).sum(dim=1))
+                del nr
+            sig_n = sn.double().cpu().numpy()
+            del w1f, sn
+        ea = chain_activation(sp.ndtri(p), sig_h, sig_n, cfg.act, chain_batch, chain_mode)
+        ea = torch.from_numpy(ea.astype(np.float32)).to(device)
+        glue_center = (ea.unsqueeze(0) @ dn_val).squeeze(0).contiguous()
+        del ea
+    del m_val, dn_val
     if cfg.act in ("relu", "sqrelu"):
         up, s_up, gate, s_gate = m_w, m_s, None, None
     elif cfg.act == "reglu":
@@ -290,7 +375,7 @@ def make_layer(cfg: StackConfig, layer: int, master: int = 0, device="cpu") -> L
         raise ValueError(cfg.act)
     return Layer(d=d, ffn=ffn, rank=r, act=cfg.act, wtype=cfg.wtype, threshold=0.0,
                  w_up=up, w_gate=gate, w_down_t=dn_w, s_up=s_up, s_gate=s_gate, s_down=dn_s,
-                 b=b, p_w1=p_w1, p_w2=p_w2, p_b=p_b, p=p, mean=mean, alpha=alpha)
+                 b=b, p_w1=p_w1, p_w2=p_w2, p_b=p_b, p=p, mean=mean, alpha=alpha, glue_center=glue_center)
 
 
 def make_tokens(cfg: StackConfig, count: int, master: int = 0, device="cpu", stream: int = 0) -> torch.Tensor:

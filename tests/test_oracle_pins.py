@@ -407,3 +407,119 @@ def test_glue_properties():
                                    rtol=2.0 ** -11, atol=2.0 ** -24)
     out32 = oracle.glue(y, x_prev.astype(np.float32))
     assert out32.dtype == np.float32
+
+
+# ------------------------------------------------------------------------------- band
+
+def _num(v):
+    return float(v) if not isinstance(v, str) else {"inf": np.inf, "-inf": -np.inf, "nan": np.nan}[v]
+
+
+def test_golden_band():
+    """The exclusion band: strict |v - theta| < 1e-4 in float64, on hand-worked values
+    (exactly 1e-4 away is outside; 5e-5 off a nonzero theta is inside; inf and NaN are outside)."""
+    g = _golden("band.json")
+    for case in g["cases"]:
+        v = np.array([_num(x) for x in case["v"]], dtype=np.float64)
+        np.testing.assert_array_equal(oracle.band(v, case["theta"]), case["band"])
+        # the same values as a [1][F] batch give the same answer row-wise
+        np.testing.assert_array_equal(oracle.band(v[None, :], case["theta"])[0], case["band"])
+    c = g["float32_case"]
+    np.testing.assert_array_equal(oracle.band(np.array(c["v"], dtype=np.float32), c["theta"]), c["band"])
+    assert oracle.THRESHOLD_BAND == 1e-4
+
+
+# ------------------------------------------------------------------------------ stacks
+
+def _golden_stack_layers(g, hot_prefix=0):
+    a, b = g["layer_a"], g["layer_b"]
+    A = _layer_dict("relu", a["w_up"], a["b"], a["w_down_t"], glue_center=np.array(a["glue_center"], float))
+    B = _layer_dict("relu", b["w_up"], b["b"], b["w_down_t"], rank=1,
+                    p_w1=np.array(b["p_w1"], float), p_w2=np.array(b["p_w2"], float),
+                    p_b=np.array(b["p_b"], float), glue_center=np.array(b["glue_center"], float),
+                    hot_prefix=hot_prefix)
+    return A, B
+
+
+def test_golden_stack_two_layers():
+    """stack_forward on a hand-worked two-layer, two-token stack (chaining vector, all-zero
+    pass-through, a predictor miss, union against per-token batches), and the same numbers
+    from an explicit layer_forward -> glue loop."""
+    g = _golden("stack_two_layers.json")
+    A, B = _golden_stack_layers(g)
+    x0 = np.array(g["x0"], dtype=np.float16)
+    # one token at a time
+    for t in range(2):
+        res = oracle.stack_forward([A, B], x0[t:t + 1])
+        np.testing.assert_array_equal(res[0]["x"][0], x0[t])
+        np.testing.assert_array_equal(res[0]["y"][0], g["y_a"][t])
+        np.testing.assert_array_equal(res[0]["mask"][0], g["mask_a"][t])
+        np.testing.assert_array_equal(res[1]["x"][0], g["x1"][t])
+        assert res[1]["x"].dtype == np.float16
+        np.testing.assert_array_equal(res[1]["v"][0], g["v_b"][t])
+        np.testing.assert_array_equal(res[1]["mask"][0], g["mask_b"][t])
+        np.testing.assert_array_equal(res[1]["y"][0], g["y_b_per_token"][t])
+    # both tokens as one batch (union of the batch's masks)
+    res = oracle.stack_forward([A, B], x0)
+    np.testing.assert_array_equal(res[1]["x"], g["x1"])
+    np.testing.assert_array_equal(res[1]["y"], g["y_b_batch"])
+    assert [r["n_active"] for r in res] == g["n_active_batch"]
+    # the explicit loop with the golden's own numbers
+    r0 = oracle.layer_forward(A, x0)
+    x1 = oracle.glue(r0["y"], x0, np.array(g["layer_a"]["glue_center"], float))
+    np.testing.assert_array_equal(x1, g["x1"])
+    r1 = oracle.layer_forward(B, x1)
+    np.testing.assert_array_equal(r1["y"], res[1]["y"])
+
+
+def test_glue_center_identities():
+    """glue(y, c) = glue(y - c, 0) whenever y is not all zero; c = 0 is the plain rms glue;
+    a token with y == c, or y == 0 while c != 0, passes x through."""
+    rng = np.random.default_rng(21)
+    d = 128
+    y = rng.normal(0, 2.0, size=(4, d))
+    c = rng.normal(0, 0.5, size=d)
+    x_prev = rng.normal(size=(4, d)).astype(np.float16)
+    y[1] = c
+    y[2] = 0.0
+    out = oracle.glue(y, x_prev, c)
+    np.testing.assert_array_equal(out[1], x_prev[1])
+    np.testing.assert_array_equal(out[2], x_prev[2])
+    for t in (0, 3):
+        np.testing.assert_array_equal(out[t], oracle.glue(y[t:t + 1] - c, x_prev[t:t + 1])[0])
+        np.testing.assert_array_equal(oracle.glue(y[t:t + 1], x_prev[t:t + 1], np.zeros(d))[0],
+                                      oracle.glue(y[t:t + 1], x_prev[t:t + 1])[0])
+        u = y[t] - c
+        np.testing.assert_allclose(out[t].astype(np.float64), u / np.sqrt(np.mean(u * u)),
+                                   rtol=2.0 ** -11, atol=2.0 ** -24)
+
+
+# ------------------------------------------------------------------------ hot prefix
+
+def test_hot_prefix_taken_without_prediction():
+    """A hot prefix of H stored neurons is always computed: H = ffn gives the dense FFN (the
+    true mask, textbook numpy), H = 0 the predictor's mask, and in between the prefix's
+    exact ReLU plus the predicted tail. Prefix decisions are +inf, never in the band."""
+    cfg = scaled(CONFIGS["opt6.7b"], d=64, ffn=128, rank=16)
+    H = make_layer(cfg, 3).to_host()
+    x = np.random.default_rng(5).normal(size=(3, 64)).astype(np.float16)
+    x64 = x.astype(np.float64)
+    w_up = H["w_up"].astype(np.float64)
+    w_dn = H["w_down_t"].astype(np.float64)
+    b = H["b"].astype(np.float64)
+    relu = np.maximum(x64 @ w_up.T + b, 0.0)
+    dense = relu @ w_dn
+    pred = oracle.predictor_logits(H, x) > 0
+    for hp in (0, 40, 128):
+        L = dict(H, hot_prefix=hp)
+        v = oracle.decision_values(L, x)
+        assert np.all(np.isinf(v[:, :hp])) and not np.any(oracle.band(v[:, :hp]))
+        m = pred.copy()
+        m[:, :hp] = True
+        for t in range(3):
+            r = oracle.layer_forward(L, x[t:t + 1])
+            np.testing.assert_array_equal(r["mask"][0], m[t])
+            np.testing.assert_allclose(r["y"][0], (m[t] * relu[t]) @ w_dn, rtol=0, atol=1e-12)
+        if hp == 128:
+            r = oracle.layer_forward(L, x)
+            np.testing.assert_allclose(r["y"], dense, rtol=0, atol=1e-12)
