@@ -14,10 +14,10 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import ACT, KERNEL_CLASSES, MASK_MODE, PI_OK, WTYPE, FfnDesc, PiError, _ptr, lib
+from ._lib import ACT, KERNEL_CLASSES, MASK_MODE, PI_OK, WTYPE, FfnDesc, PiError, StackDump, _ptr, lib
 
 __all__ = ["Context", "Ffn", "PiError", "predict", "sparse_ffn", "layer", "compact", "glue", "stack_run",
-           "stack_profile", "KERNEL_CLASSES",
+           "stack_run_dump", "stack_profile", "KERNEL_CLASSES",
            "hot_first_order", "permute_rows", "lib"]
 
 
@@ -56,24 +56,31 @@ class Context:
             pass
 
 
+def _desc(layer, neuron_table=None) -> FfnDesc:
+    """The C descriptor of a layer object (see :class:`Ffn`)."""
+    return FfnDesc(
+        d=layer.d, ffn=layer.ffn, rank=layer.rank, act=ACT[layer.act], wtype=WTYPE[layer.wtype],
+        threshold=float(layer.threshold),
+        w_up=_ptr(layer.w_up), w_gate=_ptr(layer.w_gate), w_down_t=_ptr(layer.w_down_t),
+        s_up=_ptr(layer.s_up), s_gate=_ptr(layer.s_gate), s_down=_ptr(layer.s_down),
+        b=_ptr(layer.b), p_w1=_ptr(layer.p_w1), p_w2=_ptr(layer.p_w2), p_b=_ptr(layer.p_b),
+        neuron_table=_ptr(neuron_table), hot_prefix=int(getattr(layer, "hot_prefix", 0) or 0),
+        y_center=_ptr(getattr(layer, "glue_center", None)))
+
+
 class Ffn:
     """A pi_ffn: a layer description over borrowed device tensors.
 
     ``layer`` is any object with the fields of a layer (d, ffn, rank, act, wtype,
-    threshold, w_up, w_gate, w_down_t, s_up, s_gate, s_down, b, p_w1, p_w2, p_b);
-    its tensors must stay alive as long as this object."""
+    threshold, w_up, w_gate, w_down_t, s_up, s_gate, s_down, b, p_w1, p_w2, p_b, and
+    optionally hot_prefix and glue_center); its tensors must stay alive as long as this
+    object."""
 
     def __init__(self, ctx: Context, layer, neuron_table: Optional[torch.Tensor] = None):
         self.ctx = ctx
         self.layer = layer
         self.neuron_table = neuron_table
-        desc = FfnDesc(
-            d=layer.d, ffn=layer.ffn, rank=layer.rank, act=ACT[layer.act], wtype=WTYPE[layer.wtype],
-            threshold=float(layer.threshold),
-            w_up=_ptr(layer.w_up), w_gate=_ptr(layer.w_gate), w_down_t=_ptr(layer.w_down_t),
-            s_up=_ptr(layer.s_up), s_gate=_ptr(layer.s_gate), s_down=_ptr(layer.s_down),
-            b=_ptr(layer.b), p_w1=_ptr(layer.p_w1), p_w2=_ptr(layer.p_w2), p_b=_ptr(layer.p_b),
-            neuron_table=_ptr(neuron_table))
+        desc = _desc(layer, neuron_table)
         h = c_void_p()
         ctx.check(lib().pi_ffn_create(ctx.handle, ctypes.byref(desc), ctypes.byref(h)))
         self.handle = h
@@ -112,8 +119,9 @@ def compact(ctx: Context, v: torch.Tensor, threshold: float, mask: torch.Tensor,
                                _ptr(n_active)))
 
 
-def glue(ctx: Context, y: torch.Tensor, x_prev: torch.Tensor, x_out: torch.Tensor):
-    ctx.check(lib().pi_glue(ctx.handle, _ptr(y), _ptr(x_prev), y.shape[0], y.shape[1],
+def glue(ctx: Context, y: torch.Tensor, x_prev: torch.Tensor, x_out: torch.Tensor,
+         center: Optional[torch.Tensor] = None):
+    ctx.check(lib().pi_glue(ctx.handle, _ptr(y), _ptr(center), _ptr(x_prev), y.shape[0], y.shape[1],
                             int(x_prev.dtype == torch.float32), _ptr(x_out)))
 
 
@@ -122,6 +130,19 @@ def stack_run(ctx: Context, ffns: Sequence[Ffn], x_tokens: torch.Tensor, batch: 
     arr = (c_void_p * len(ffns))(*[f.handle.value for f in ffns])
     ctx.check(lib().pi_stack_run(ctx.handle, arr, len(ffns), _ptr(x_tokens), x_tokens.shape[0], batch, _ptr(y_out),
                                  _ptr(n_active_log), int(bool(use_graph))))
+
+
+def stack_run_dump(ctx: Context, ffns: Sequence[Ffn], x_tokens: torch.Tensor, batch: int, y_out: torch.Tensor,
+                   n_active_log: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
+                   mask: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                   n: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, ffn_stride: int = 0):
+    """stack_run recording every (step, layer): x [S][L][B][d], mask [S][L][B][stride/64] int64,
+    idx [S][L][stride] int32, n [S][L] int32, y [S][L][B][d] fp32 (each optional)."""
+    arr = (c_void_p * len(ffns))(*[f.handle.value for f in ffns])
+    stride = ffn_stride or max(f.layer.ffn for f in ffns)
+    dump = StackDump(x=_ptr(x), mask=_ptr(mask), idx=_ptr(idx), n=_ptr(n), y=_ptr(y), ffn_stride=stride)
+    ctx.check(lib().pi_stack_run_dump(ctx.handle, arr, len(ffns), _ptr(x_tokens), x_tokens.shape[0], batch,
+                                      _ptr(y_out), _ptr(n_active_log), ctypes.byref(dump)))
 
 
 def stack_profile(ctx: Context, ffns: Sequence[Ffn], x_tokens: torch.Tensor, batch: int, y_out: torch.Tensor,

@@ -26,8 +26,13 @@ class FfnDesc(ctypes.Structure):
         ("w_up", c_void_p), ("w_gate", c_void_p), ("w_down_t", c_void_p),
         ("s_up", c_void_p), ("s_gate", c_void_p), ("s_down", c_void_p),
         ("b", c_void_p), ("p_w1", c_void_p), ("p_w2", c_void_p), ("p_b", c_void_p),
-        ("neuron_table", c_void_p),
+        ("neuron_table", c_void_p), ("hot_prefix", c_int32), ("y_center", c_void_p),
     ]
+
+
+class StackDump(ctypes.Structure):
+    _fields_ = [("x", c_void_p), ("mask", c_void_p), ("idx", c_void_p), ("n", c_void_p), ("y", c_void_p),
+                ("ffn_stride", c_int32)]
 
 
 _SIGS = {
@@ -44,9 +49,11 @@ _SIGS = {
     "pi_sparse_ffn": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "pi_layer": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "pi_compact": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p]),
-    "pi_glue": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p]),
+    "pi_glue": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p]),
     "pi_stack_run": (c_int32, [c_void_p, POINTER(c_void_p), c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                c_void_p, c_int32]),
+    "pi_stack_run_dump": (c_int32, [c_void_p, POINTER(c_void_p), c_int32, c_void_p, c_int32, c_int32, c_void_p,
+                                    c_void_p, POINTER(StackDump)]),
     "pi_stack_profile": (c_int32, [c_void_p, POINTER(c_void_p), c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                    c_void_p, POINTER(c_double), POINTER(c_int64)]),
     "pi_hot_first_order": (c_int32, [POINTER(c_double), c_int32, POINTER(c_int32)]),

@@ -9,8 +9,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpi.so")
 SOURCES = [os.path.join(CSRC, "pi_lib.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("pi_device.hpp", "pi_kernels.hpp")] + \
-    [os.path.join(ROOT, "include", "pi.h")]
 
 
 def hipcc() -> str:

@@ -44,6 +44,7 @@ __device__ __forceinline__ float act_one_rt(int act, float h) {
 
 struct LayerDev {
   int d, ffn, rank, act, wtype;
+  int hot_prefix;  // stored neurons [0, hot_prefix) are taken without a prediction (predictor layers)
   float threshold;
   const uint8_t *w_up, *w_gate, *w_down_t;
   const uint16_t *s_up, *s_gate, *s_down;
@@ -54,16 +55,19 @@ struct LayerDev {
 
 // Where a kernel's input vector x comes from.
 //  y == nullptr: x is given ([B][d], fp16 or fp32 storage).
-//  y != nullptr: glue between stacked layers, x = round(y / sqrt(mean(y^2))) per token, or
-//                x_prev (= x) unchanged when y is all zero; workgroup 0 stores it to x_out.
-//                y is the sum of ny partial sums y[g * ystride + t * d + c] (ny >= 1), added
-//                in order g = 0, 1, ... (the previous layer's down projection leaves them).
+//  y != nullptr: glue between stacked layers. Per token, u = y - c and
+//                x = round(u / sqrt(mean(u^2))), or x_prev (= x) unchanged when y (or u) is
+//                all zero; workgroup 0 stores it to x_out. c ([d] fp32, the previous layer's
+//                expected output) may be NULL (zero). y is the sum of ny partial sums
+//                y[g * ystride + t * d + col] (ny >= 1), added in order g = 0, 1, ... (the
+//                previous layer's down projection leaves them).
 struct XIn {
   const void* x;
   const float* y;
   void* x_out;
   int ny;
   int ystride;
+  const float* c;
 };
 
 // Element (t, c) of the glue's y, its partial sums added in order.
@@ -91,22 +95,56 @@ __device__ __forceinline__ u32x4 y4_at(const XIn& in, size_t tc) {
 template <bool XF32> struct XType { typedef half_t T; };
 template <> struct XType<true> { typedef float T; };
 
-// Per-token rms of y (0 for an all-zero y) into rms_s[NB].
+// Block-wide sums of two floats per thread (BLOCK threads). Uses `red` [2 * NWAVES] in LDS.
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  __syncthreads();
+  if (lane == 0) {
+    red[w] = a;
+    red[NWAVES + w] = b;
+  }
+  __syncthreads();
+  a = 0.f;
+  b = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    a += red[i];
+    b += red[NWAVES + i];
+  }
+}
+
+// The glue's divisor from the sums of squares of y and of u = y - c: sqrt(mean(u^2)), or 0
+// (x passes through) when either is zero.
+__device__ __forceinline__ float glue_divisor(float ss_y, float ss_u, int d) {
+  return (ss_y == 0.f || ss_u == 0.f) ? 0.f : sqrtf(ss_u / (float)d);
+}
+
+// Four consecutive elements of the center c from column col (zeros when c is NULL).
+__device__ __forceinline__ u32x4 c4_at(const XIn& in, int col) {
+  return in.c != nullptr ? ld16(in.c + col) : (u32x4){0, 0, 0, 0};
+}
+
+// Per-token divisor of the glue (0: pass x through) into rms_s[NB]. `red` [2 * NWAVES].
 template <int NB>
 __device__ __forceinline__ void glue_rms(const XIn& in, int B, int d, float* rms_s, float* red) {
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
-    float ss = 0.f;
+    float ss = 0.f, su = 0.f;
     if (t < B)
       for (int c = threadIdx.x * 4; c < d; c += BLOCK * 4) {
         const u32x4 v = y4_at(in, (size_t)t * d + c);
-        ss = fmaf(u2f(v[0]), u2f(v[0]), ss);
-        ss = fmaf(u2f(v[1]), u2f(v[1]), ss);
-        ss = fmaf(u2f(v[2]), u2f(v[2]), ss);
-        ss = fmaf(u2f(v[3]), u2f(v[3]), ss);
+        const u32x4 cv = c4_at(in, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float yv = u2f(v[e]), uv = yv - u2f(cv[e]);
+          ss = fmaf(yv, yv, ss);
+          su = fmaf(uv, uv, su);
+        }
       }
-    ss = block_sum(ss, red);
-    if (threadIdx.x == 0) rms_s[t] = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
+    block_sum2(ss, su, red);
+    if (threadIdx.x == 0) rms_s[t] = glue_divisor(ss, su, d);
   }
   __syncthreads();
 }
@@ -128,6 +166,13 @@ template <int NB, typename XT, int J = GLUE_J, typename Hook = NoHook>
 __device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int ldx, float* red, bool store_out,
                                        Hook after_issue = Hook()) {
   const int n4 = d >> 2;
+  // the center's chunks (the same for every token), issued before the first y loads
+  u32x4 cv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = threadIdx.x + BLOCK * j;
+    cv[j] = (in.c != nullptr) ? ld16_or0(in.c + 4 * min(c, n4 - 1), c < n4) : (u32x4){0, 0, 0, 0};
+  }
   for (int t = 0; t < NB; ++t) {
     if (t >= B) {
       for (int c = threadIdx.x; c < d; c += BLOCK) xs[t * ldx + c] = (XT)0.f;
@@ -171,16 +216,19 @@ __device__ __forceinline__ void glue_x(const XIn& in, int B, int d, XT* xs, int 
         }
       }
     }
-    float ss = 0.f;
+    // sums of squares of y and of u = y - c (v becomes u); chunks past d are zero in both
+    float ss = 0.f, su = 0.f;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      ss = fmaf(u2f(v[j][0]), u2f(v[j][0]), ss);
-      ss = fmaf(u2f(v[j][1]), u2f(v[j][1]), ss);
-      ss = fmaf(u2f(v[j][2]), u2f(v[j][2]), ss);
-      ss = fmaf(u2f(v[j][3]), u2f(v[j][3]), ss);
-    }
-    ss = block_sum(ss, red);
-    const float r = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float yv = u2f(v[j][e]), uv = yv - u2f(cv[j][e]);
+        ss = fmaf(yv, yv, ss);
+        su = fmaf(uv, uv, su);
+        v[j][e] = __builtin_bit_cast(uint32_t, uv);
+      }
+    block_sum2(ss, su, red);
+    const float r = glue_divisor(ss, su, d);
     const XT* xp = reinterpret_cast<const XT*>(in.x) + (size_t)t * d;
     XT* xo = reinterpret_cast<XT*>(in.x_out) + (size_t)t * d;
     // r is the same in every thread: one branch, so the common case issues no load of x_prev
@@ -220,7 +268,7 @@ __device__ __forceinline__ void stage_x(const XIn& in, int B, int d, int c0, int
         if (in.y != nullptr) {
           const float r = rms_s[t];
           if (r == 0.f) v = reinterpret_cast<const XT*>(in.x)[gi];
-          else v = (XT)(y_at(in, gi) / r);
+          else v = (XT)((y_at(in, gi) - (in.c != nullptr ? in.c[c0 + c] : 0.f)) / r);
           if (store_out) reinterpret_cast<XT*>(in.x_out)[gi] = v;
         } else {
           v = reinterpret_cast<const XT*>(in.x)[gi];
@@ -549,7 +597,7 @@ template <int NB>
 __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, int dc, float* __restrict__ z) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);
-  __shared__ float red[NWAVES];
+  __shared__ float red[2 * NWAVES];
   __shared__ float rms_s[NB];
   const int d = L.d, r = L.rank;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
@@ -654,13 +702,18 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
   const int byte = wave * gridDim.x + blockIdx.x;  // this wave's byte of the mask
   const int row0 = byte * RPT;                      // its first neuron
   const uint8_t* w2 = reinterpret_cast<const uint8_t*>(L.p_w2);
+  // A byte wholly inside the hot prefix reads no predictor rows: its loads all go to the
+  // first row's first chunks (one cached line per lane) and are dropped. The loads stay
+  // unconditional, so they are all in flight at once.
+  const bool all_hot = row0 + RPT <= L.hot_prefix;
   u32x4 w[RPT][CPL];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + WAVE * j;
-      w[i][j] = ld_stream_or0(w2 + ((size_t)(row0 + i) * r + min(c, nch - 1) * 8) * 2, c < nch);
+      const size_t off = all_hot ? (size_t)min(c, nch - 1) * 8 : (size_t)(row0 + i) * r + min(c, nch - 1) * 8;
+      w[i][j] = ld_stream_or0(w2 + off * 2, c < nch && !all_hot);
     }
   // z as fp16 pairs hi + lo. At 8 tokens without the fused activations they are staged once
   // per workgroup in LDS ([NB][r/2] words each): in registers they took 128 VGPRs and left
@@ -757,7 +810,10 @@ __global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __res
         }
       acc[i] = sum;
     }
-    const float v = transpose_reduce<RPT>(acc, lane) + bias;
+    // hot-prefix neurons are always taken: decision value +inf (the reduction runs in every
+    // lane: its shuffles need the whole wave)
+    const float vr = transpose_reduce<RPT>(acc, lane) + bias;
+    const float v = (row0 + (lane & (RPT - 1)) < L.hot_prefix) ? __builtin_inff() : vr;
     if (t < B) {
       const uint32_t bits = (uint32_t)__ballot(lane < RPT && v > L.threshold) & ((1u << RPT) - 1);
       ubits |= bits;
@@ -793,7 +849,7 @@ __global__ __launch_bounds__(BLOCK) void k_truemask(LayerDev L, XIn xin, int B, 
   typedef typename XType<XF32>::T XT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
-  __shared__ float red[NWAVES];
+  __shared__ float red[2 * NWAVES];
   __shared__ float vs[NB][WAVE];
   __shared__ uint64_t s_union;
   const int d = L.d, ffn = L.ffn;
@@ -1424,31 +1480,41 @@ __global__ __launch_bounds__(BLOCK) void k_reduce(const float* __restrict__ part
   if (wave == 0 && i < BD) y[i] = (s4[0][lane] + s4[1][lane]) + (s4[2][lane] + s4[3][lane]);
 }
 
-// Standalone glue: one workgroup per token, d % 4 == 0. Each thread issues all of its
-// 16-byte loads of y (up to GLUE_J) before using them; longer rows take further passes.
+// Standalone glue: one workgroup per token, d % 4 == 0: u = y - c (c nullable), x_out =
+// round(u / sqrt(mean(u^2))), or x_prev when y or u is all zero. Each thread issues all of
+// its 16-byte loads of y and c (up to GLUE_J each) before using them; longer rows take
+// further passes.
 template <bool XF32>
-__global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, const void* __restrict__ x_prev, int d,
-                                                void* __restrict__ x_out) {
+__global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, const float* __restrict__ center,
+                                                const void* __restrict__ x_prev, int d, void* __restrict__ x_out) {
   typedef typename XType<XF32>::T XT;
-  __shared__ float red[NWAVES];
+  __shared__ float red[2 * NWAVES];
   const int t = blockIdx.x;
   const float* yt = y + (size_t)t * d;
   const int n4 = d >> 2;
-  float ss = 0.f;
-  for (int c0 = 0; c0 < n4; c0 += BLOCK * GLUE_J) {
-    u32x4 v[GLUE_J];
+  auto load = [&](int c0, u32x4 (&v)[GLUE_J], u32x4 (&cv)[GLUE_J]) {
 #pragma unroll
     for (int j = 0; j < GLUE_J; ++j) {
       const int c = c0 + threadIdx.x + BLOCK * j;
-      v[j] = (c < n4) ? ld16(yt + 4 * c) : (u32x4){0, 0, 0, 0};
+      v[j] = ld16_or0(yt + 4 * min(c, n4 - 1), c < n4);
+      cv[j] = center != nullptr ? ld16_or0(center + 4 * min(c, n4 - 1), c < n4) : (u32x4){0, 0, 0, 0};
     }
+  };
+  float ss = 0.f, su = 0.f;
+  for (int c0 = 0; c0 < n4; c0 += BLOCK * GLUE_J) {
+    u32x4 v[GLUE_J], cv[GLUE_J];
+    load(c0, v, cv);
 #pragma unroll
     for (int j = 0; j < GLUE_J; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ss = fmaf(u2f(v[j][e]), u2f(v[j][e]), ss);
+      for (int e = 0; e < 4; ++e) {
+        const float yv = u2f(v[j][e]), uv = yv - u2f(cv[j][e]);
+        ss = fmaf(yv, yv, ss);
+        su = fmaf(uv, uv, su);
+      }
   }
-  ss = block_sum(ss, red);
-  const float r = (ss == 0.f) ? 0.f : sqrtf(ss / (float)d);
+  block_sum2(ss, su, red);
+  const float r = glue_divisor(ss, su, d);
   const XT* xp = reinterpret_cast<const XT*>(x_prev) + (size_t)t * d;
   XT* xo = reinterpret_cast<XT*>(x_out) + (size_t)t * d;
   if (r == 0.f) {  // all-zero y: x passes through (r is the same in every thread)
@@ -1456,18 +1522,14 @@ __global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, con
     return;
   }
   for (int c0 = 0; c0 < n4; c0 += BLOCK * GLUE_J) {
-    u32x4 v[GLUE_J];
-#pragma unroll
-    for (int j = 0; j < GLUE_J; ++j) {
-      const int c = c0 + threadIdx.x + BLOCK * j;
-      v[j] = ld16_or0(yt + 4 * min(c, n4 - 1), c < n4);
-    }
+    u32x4 v[GLUE_J], cv[GLUE_J];
+    load(c0, v, cv);
 #pragma unroll
     for (int j = 0; j < GLUE_J; ++j) {
       const int c = c0 + threadIdx.x + BLOCK * j;
       if (c < n4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xo[4 * c + e] = (XT)(u2f(v[j][e]) / r);
+        for (int e = 0; e < 4; ++e) xo[4 * c + e] = (XT)((u2f(v[j][e]) - u2f(cv[j][e])) / r);
     }
   }
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -50,7 +51,7 @@ struct pi_ctx {
   // the null stream, which cannot be captured) and launched on the caller's stream
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t gexec = nullptr;
-  std::vector<const pi_ffn*> g_layers;
+  std::vector<uint64_t> g_layers;  // serial numbers of the captured step's layers
   int g_B = 0;
   // per-kernel event timing (pi_stack_profile only)
   bool profiling = false;
@@ -62,7 +63,10 @@ struct pi_ctx {
 struct pi_ffn {
   pi_ffn_desc desc;
   pi_ctx* ctx;
+  uint64_t serial;  // unique per pi_ffn_create in this process: the key of a captured stack step
 };
+
+static std::atomic<uint64_t> g_ffn_serial{1};
 
 namespace {
 
@@ -130,6 +134,7 @@ LayerDev to_dev(const pi_ffn_desc& d) {
   L.d = d.d;
   L.ffn = d.ffn;
   L.rank = d.rank;
+  L.hot_prefix = d.hot_prefix;
   L.act = d.act;
   L.wtype = d.wtype;
   L.threshold = d.threshold;
@@ -146,7 +151,7 @@ LayerDev to_dev(const pi_ffn_desc& d) {
   return L;
 }
 
-int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+constexpr int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
 size_t x_elem(int wtype) { return wtype == PI_W_F32 ? 4 : 2; }
 
 template <typename K>
@@ -322,8 +327,8 @@ pi_status launch_up(pi_ctx* c, const LayerDev& L, const void* x, int B, const in
 // 0/+2/+4% at 1/2/4 tokens; Llama-2-70B +1/+2/+2%; OPT-6.7B (d = 4096) -10/-8/-5% at 1/2/4
 // tokens and +19% at 8. Slices are sw columns wide, a multiple of 512 whose x fits the budget.
 constexpr int UPC_WGS_PER_CU = 2;
-bool up_cols(int NB, int d, size_t xe) { return (size_t)NB * d * xe > X_LDS_BUDGET; }
-int up_cols_width(int NB, size_t xe) { return (int)(X_LDS_BUDGET / (NB * xe)) / 512 * 512; }
+constexpr bool up_cols(int NB, int d, size_t xe) { return (size_t)NB * d * xe > X_LDS_BUDGET; }
+constexpr int up_cols_width(int NB, size_t xe) { return (int)(X_LDS_BUDGET / (NB * xe)) / 512 * 512; }
 size_t x_elem(const LayerDev& L) { return L.wtype == W_F32 ? 4 : 2; }
 bool use_up_cols(const LayerDev& L, int B) {
   const int NB = nb_for(B);
@@ -332,13 +337,15 @@ bool use_up_cols(const LayerDev& L, int B) {
 
 // Floats of hp for a context's limits: the largest slices x 2 rows x tokens x ffn over the
 // batch classes and element sizes that take the column-sliced path.
-size_t up_cols_floats(int max_batch, int max_d, int max_ffn) {
+constexpr size_t up_cols_floats(int max_batch, int max_d, int max_ffn) {
   size_t m = 0;
-  for (int NB = 1; NB <= std::min(8, nb_for(std::min(max_batch, 8))); NB *= 2)
-    for (size_t xe : {(size_t)2, (size_t)4})
+  const int nb_max = nb_for(max_batch < 8 ? max_batch : 8);
+  for (int NB = 1; NB <= nb_max; NB *= 2)
+    for (size_t xe = 2; xe <= 4; xe += 2)
       if (up_cols(NB, max_d, xe)) {
         const int sw = up_cols_width(NB, xe);
-        m = std::max(m, (size_t)((max_d + sw - 1) / sw) * 2 * NB * max_ffn);
+        const size_t f = (size_t)((max_d + sw - 1) / sw) * 2 * NB * max_ffn;
+        m = f > m ? f : m;
       }
   return m;
 }
@@ -472,12 +479,91 @@ pi_status launch_down(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in
   }
 }
 
+// Forget the cached stack step (it holds the layers' weight pointers and the context's mode).
+void drop_graph(pi_ctx* c) {
+  if (c->gexec != nullptr) (void)hipGraphExecDestroy(c->gexec);
+  c->gexec = nullptr;
+  c->g_layers.clear();
+  c->g_B = 0;
+}
+
 pi_status launch_compact(pi_ctx* c, int ffn, int32_t* idx, int32_t* n) {
   const int W = ffn / 64;
   hipLaunchKernelGGL(k_compact, dim3((W + BLOCK - 1) / BLOCK), dim3(BLOCK), 0, c->stream, c->munion, W, idx, n,
                      (int32_t*)nullptr);
   PI_HIP(c, hipGetLastError());
   return PI_OK;
+}
+
+// ---------------------------------------------------------------- scratch layout
+
+// Byte offsets of the scratch buffers in one block (each 256-byte aligned), for batches up to
+// max_batch tokens and layers up to max_d x max_ffn with rank up to max_rank. `stack`: also
+// the stack runner's x buffers and count log. Batches above 8 tokens add the matrix-core
+// path's buffers.
+struct WsLayout {
+  size_t z, mt, mu, idx, n, a, hp, part, y, x0, x1, xs, nlog, zp, zh, zl, a16, total;
+  size_t hp_floats, lda;
+  bool mm;
+};
+
+constexpr size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+constexpr WsLayout ws_layout(int max_batch, int max_d, int max_ffn, int max_rank, bool stack) {
+  WsLayout o{};
+  const size_t B = max_batch, D = max_d, F = max_ffn, R = max_rank > 8 ? max_rank : 8;
+  const size_t nbv = (size_t)nb_for(max_batch < 8 ? max_batch : 8);
+  o.mm = max_batch > 8;
+  size_t off = 0;
+  o.z = off; off += al256(B * R * 4);
+  o.mt = off; off += al256(B * (F / 64) * 8);
+  o.mu = off; off += al256((F / 64) * 8);
+  o.idx = off; off += al256(F * 4);
+  o.n = off; off += al256(16 * 4);
+  o.a = off; off += al256((B > nbv ? B : nbv) * F * 4);
+  o.hp_floats = up_cols_floats(max_batch, max_d, max_ffn);
+  o.hp = off; off += al256(o.hp_floats * 4);
+  const size_t groups = o.mm ? (DOWN_G_WIDE > MM_KSD ? DOWN_G_WIDE : MM_KSD) : DOWN_G_WIDE;
+  o.part = off; off += al256(groups * B * D * 4);
+  o.y = off; off += al256(B * D * 4);
+  o.x0 = off; off += stack ? al256(B * D * 4) : 0;
+  o.x1 = off; off += stack ? al256(B * D * 4) : 0;
+  o.xs = off; off += stack ? al256(B * D * 4) : 0;
+  o.nlog = off; off += stack ? al256(NLOG_CAP * 4) : 0;
+  o.lda = (F + 15) / 16 * 16;
+  o.zp = off; off += o.mm ? al256((size_t)MM_KS1 * B * R * 4) : 0;
+  o.zh = off; off += o.mm ? al256(B * R * 2) : 0;
+  o.zl = off; off += o.mm ? al256(B * R * 2) : 0;
+  o.a16 = off; off += o.mm ? al256((size_t)(B > 32 ? 64 : 32) * o.lda * 2) : 0;
+  o.total = off;
+  return o;
+}
+
+// Point a context's scratch fields into the block at ws laid out by o.
+void ws_assign(pi_ctx* c, uint8_t* ws, const WsLayout& o) {
+  c->ws = ws;
+  c->ws_bytes = o.total;
+  c->z = reinterpret_cast<float*>(ws + o.z);
+  c->mtok = reinterpret_cast<uint64_t*>(ws + o.mt);
+  c->munion = reinterpret_cast<uint64_t*>(ws + o.mu);
+  c->idx = reinterpret_cast<int32_t*>(ws + o.idx);
+  c->nbuf = reinterpret_cast<int32_t*>(ws + o.n);
+  c->a = reinterpret_cast<float*>(ws + o.a);
+  c->hp = reinterpret_cast<float*>(ws + o.hp);
+  c->hp_cap = o.hp_floats;
+  c->part = reinterpret_cast<float*>(ws + o.part);
+  c->y = reinterpret_cast<float*>(ws + o.y);
+  c->xbuf[0] = ws + o.x0;
+  c->xbuf[1] = ws + o.x1;
+  c->xstage = ws + o.xs;
+  c->nlog = reinterpret_cast<int32_t*>(ws + o.nlog);
+  if (o.mm) {
+    c->zpart = reinterpret_cast<float*>(ws + o.zp);
+    c->zhi = reinterpret_cast<half_t*>(ws + o.zh);
+    c->zlo = reinterpret_cast<half_t*>(ws + o.zl);
+    c->a16 = reinterpret_cast<half_t*>(ws + o.a16);
+    c->lda = (int)o.lda;
+  }
 }
 
 // ---------------------------------------------------------------- argument checks
@@ -507,6 +593,44 @@ pi_status check_dev_ptr(pi_ctx* c, const void* p, const char* name, bool nullabl
     pi_status s_ = (expr);           \
     if (s_ != PI_OK) return s_;      \
   } while (0)
+
+// A layer description against the limits of ctx (shapes, types, pointers).
+pi_status check_desc(pi_ctx* ctx, const pi_ffn_desc& d) {
+  if (d.d < 8 || d.d % 8) return fail(ctx, PI_ERR_INVALID, "d must be a positive multiple of 8 (got %d)", d.d);
+  if (d.ffn < 64 || d.ffn % 64) return fail(ctx, PI_ERR_INVALID, "ffn must be a positive multiple of 64 (got %d)", d.ffn);
+  if (d.rank < 0 || d.rank % 8) return fail(ctx, PI_ERR_INVALID, "rank must be 0 or a multiple of 8 (got %d)", d.rank);
+  if (d.rank > 1024) return fail(ctx, PI_ERR_UNSUPPORTED, "rank %d above 1024", d.rank);
+  if (d.d > ctx->max_d || d.ffn > ctx->max_ffn || d.rank > ctx->max_rank)
+    return fail(ctx, PI_ERR_INVALID, "layer %dx%d rank %d exceeds the context (%dx%d rank %d)", d.d, d.ffn, d.rank,
+                ctx->max_d, ctx->max_ffn, ctx->max_rank);
+  if (d.act != PI_ACT_RELU && d.act != PI_ACT_REGLU && d.act != PI_ACT_SQRELU)
+    return fail(ctx, PI_ERR_INVALID, "unknown activation %d", d.act);
+  if (d.wtype != PI_W_F32 && d.wtype != PI_W_F16 && d.wtype != PI_W_Q4_0)
+    return fail(ctx, PI_ERR_INVALID, "unknown weight type %d", d.wtype);
+  if (d.wtype == PI_W_Q4_0 && d.d % 32) return fail(ctx, PI_ERR_INVALID, "Q4_0 needs d %% 32 == 0 (got %d)", d.d);
+  if (d.wtype == PI_W_F32 && d.rank > 0)
+    return fail(ctx, PI_ERR_UNSUPPORTED, "the predictor runs on fp16 tokens: fp32 layers take rank 0");
+  PI_TRY(check_dev_ptr(ctx, d.w_up, "w_up"));
+  PI_TRY(check_dev_ptr(ctx, d.w_down_t, "w_down_t"));
+  PI_TRY(check_dev_ptr(ctx, d.b, "b"));
+  if (d.act == PI_ACT_REGLU) PI_TRY(check_dev_ptr(ctx, d.w_gate, "w_gate"));
+  if (d.wtype == PI_W_Q4_0) {
+    PI_TRY(check_dev_ptr(ctx, d.s_up, "s_up"));
+    PI_TRY(check_dev_ptr(ctx, d.s_down, "s_down"));
+    if (d.act == PI_ACT_REGLU) PI_TRY(check_dev_ptr(ctx, d.s_gate, "s_gate"));
+  }
+  if (d.rank > 0) {
+    PI_TRY(check_dev_ptr(ctx, d.p_w1, "p_w1"));
+    PI_TRY(check_dev_ptr(ctx, d.p_w2, "p_w2"));
+    PI_TRY(check_dev_ptr(ctx, d.p_b, "p_b"));
+  }
+  if (d.hot_prefix < 0 || d.hot_prefix > d.ffn)
+    return fail(ctx, PI_ERR_INVALID, "hot_prefix %d outside [0, ffn %d]", d.hot_prefix, d.ffn);
+  if (d.hot_prefix > 0 && d.rank == 0)
+    return fail(ctx, PI_ERR_UNSUPPORTED, "a hot prefix needs a predictor layer (rank > 0)");
+  PI_TRY(check_dev_ptr(ctx, d.y_center, "y_center", true));
+  return PI_OK;
+}
 
 // ---------------------------------------------------------------- batched path (9..64 tokens)
 
@@ -558,6 +682,7 @@ pi_status mm_predict(pi_ctx* c, const LayerDev& L, const half_t* x, int B, uint3
     q.mask_union = reinterpret_cast<uint32_t*>(c->munion);
     q.logits = logits;
     q.ffn = L.ffn;
+    q.hot_prefix = L.hot_prefix;
     return launch_mm<EPI_MASK, ACT_RELU, true>(c, q, L.ffn, 1, K_STAGE2);
   }
   // no predictor: the true pre-activation of the masked projection
@@ -713,61 +838,19 @@ pi_status pi_ctx_create(int32_t device, void* hip_stream, int32_t max_batch, int
     c->cus = prop.multiProcessorCount;
     c->lds_max = prop.sharedMemPerBlock;
   }
-  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  const size_t B = max_batch, D = max_d, F = max_ffn, R = std::max(max_rank, 8);
-  size_t off = 0;
-  const size_t o_z = off; off += al(B * R * 4);
-  const size_t o_mt = off; off += al(B * (F / 64) * 8);
-  const size_t o_mu = off; off += al((F / 64) * 8);
-  const size_t o_idx = off; off += al(F * 4);
-  const size_t o_n = off; off += al(16 * 4);
-  const size_t o_a = off; off += al(std::max(B, (size_t)nb_for(std::min(max_batch, 8))) * F * 4);
-  const size_t hp_floats = up_cols_floats(max_batch, max_d, max_ffn);
-  const size_t o_hp = off; off += al(hp_floats * 4);
-  const size_t o_part = off; off += al((size_t)std::max(DOWN_G_WIDE, MM_KSD) * B * D * 4);
-  const size_t o_y = off; off += al(B * D * 4);
-  const size_t o_x0 = off; off += al(B * D * 4);
-  const size_t o_x1 = off; off += al(B * D * 4);
-  const size_t o_xs = off; off += al(B * D * 4);
-  const size_t o_nlog = off; off += al(NLOG_CAP * 4);
-  const bool mm = max_batch > 8;
-  const size_t lda = ((size_t)F + 15) / 16 * 16;
-  const size_t o_zp = off; off += mm ? al((size_t)MM_KS1 * B * R * 4) : 0;
-  const size_t o_zh = off; off += mm ? al(B * R * 2) : 0;
-  const size_t o_zl = off; off += mm ? al(B * R * 2) : 0;
-  const size_t o_a16 = off; off += mm ? al((size_t)(B > 32 ? 64 : 32) * lda * 2) : 0;
-  if (hipMalloc(reinterpret_cast<void**>(&c->ws), off) != hipSuccess) {
+  const WsLayout o = ws_layout(max_batch, max_d, max_ffn, max_rank, true);
+  uint8_t* ws = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&ws), o.total) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return PI_ERR_OOM;
   }
-  c->ws_bytes = off;
-  if (hipMemset(c->ws, 0, off) != hipSuccess) {
-    (void)hipFree(c->ws);
+  if (hipMemset(ws, 0, o.total) != hipSuccess) {
+    (void)hipFree(ws);
     delete c;
     return PI_ERR_HIP;
   }
-  c->z = reinterpret_cast<float*>(c->ws + o_z);
-  c->mtok = reinterpret_cast<uint64_t*>(c->ws + o_mt);
-  c->munion = reinterpret_cast<uint64_t*>(c->ws + o_mu);
-  c->idx = reinterpret_cast<int32_t*>(c->ws + o_idx);
-  c->nbuf = reinterpret_cast<int32_t*>(c->ws + o_n);
-  c->a = reinterpret_cast<float*>(c->ws + o_a);
-  c->part = reinterpret_cast<float*>(c->ws + o_part);
-  c->hp = reinterpret_cast<float*>(c->ws + o_hp);
-  c->hp_cap = hp_floats;
-  c->y = reinterpret_cast<float*>(c->ws + o_y);
-  c->xbuf[0] = c->ws + o_x0;
-  c->xbuf[1] = c->ws + o_x1;
-  c->xstage = c->ws + o_xs;
-  c->nlog = reinterpret_cast<int32_t*>(c->ws + o_nlog);
-  if (mm) {
-    c->zpart = reinterpret_cast<float*>(c->ws + o_zp);
-    c->zhi = reinterpret_cast<half_t*>(c->ws + o_zh);
-    c->zlo = reinterpret_cast<half_t*>(c->ws + o_zl);
-    c->a16 = reinterpret_cast<half_t*>(c->ws + o_a16);
-    c->lda = (int)lda;
-  }
+  ws_assign(c, ws, o);
   if (hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess) {
     (void)hipFree(c->ws);
     delete c;
@@ -790,22 +873,14 @@ void pi_ctx_destroy(pi_ctx* ctx) {
 pi_status pi_ctx_set_stream(pi_ctx* ctx, void* hip_stream) {
   if (ctx == nullptr) return PI_ERR_INVALID;
   ctx->stream = static_cast<hipStream_t>(hip_stream);
-  if (ctx->gexec != nullptr) {
-    (void)hipGraphExecDestroy(ctx->gexec);
-    ctx->gexec = nullptr;
-    ctx->g_layers.clear();
-  }
+  drop_graph(ctx);
   return PI_OK;
 }
 
 pi_status pi_ctx_set_mask_mode(pi_ctx* ctx, int32_t mode) {
   if (ctx == nullptr) return PI_ERR_INVALID;
   if (mode != PI_MASK_UNION && mode != PI_MASK_PER_TOKEN) return fail(ctx, PI_ERR_INVALID, "unknown mask mode %d", mode);
-  if (mode != ctx->mask_mode && ctx->gexec != nullptr) {  // a captured stack step has the old mode baked in
-    (void)hipGraphExecDestroy(ctx->gexec);
-    ctx->gexec = nullptr;
-    ctx->g_layers.clear();
-  }
+  if (mode != ctx->mask_mode) drop_graph(ctx);  // a captured stack step has the old mode baked in
   ctx->mask_mode = mode;
   return PI_OK;
 }
@@ -815,43 +890,26 @@ pi_status pi_ffn_create(pi_ctx* ctx, const pi_ffn_desc* desc, pi_ffn** out) {
   *out = nullptr;
   if (desc == nullptr) return fail(ctx, PI_ERR_INVALID, "desc is NULL");
   const pi_ffn_desc& d = *desc;
-  if (d.d < 8 || d.d % 8) return fail(ctx, PI_ERR_INVALID, "d must be a positive multiple of 8 (got %d)", d.d);
-  if (d.ffn < 64 || d.ffn % 64) return fail(ctx, PI_ERR_INVALID, "ffn must be a positive multiple of 64 (got %d)", d.ffn);
-  if (d.rank < 0 || d.rank % 8) return fail(ctx, PI_ERR_INVALID, "rank must be 0 or a multiple of 8 (got %d)", d.rank);
-  if (d.rank > 1024) return fail(ctx, PI_ERR_UNSUPPORTED, "rank %d above 1024", d.rank);
-  if (d.d > ctx->max_d || d.ffn > ctx->max_ffn || d.rank > ctx->max_rank)
-    return fail(ctx, PI_ERR_INVALID, "layer %dx%d rank %d exceeds the context (%dx%d rank %d)", d.d, d.ffn, d.rank,
-                ctx->max_d, ctx->max_ffn, ctx->max_rank);
-  if (d.act != PI_ACT_RELU && d.act != PI_ACT_REGLU && d.act != PI_ACT_SQRELU)
-    return fail(ctx, PI_ERR_INVALID, "unknown activation %d", d.act);
-  if (d.wtype != PI_W_F32 && d.wtype != PI_W_F16 && d.wtype != PI_W_Q4_0)
-    return fail(ctx, PI_ERR_INVALID, "unknown weight type %d", d.wtype);
-  if (d.wtype == PI_W_Q4_0 && d.d % 32) return fail(ctx, PI_ERR_INVALID, "Q4_0 needs d %% 32 == 0 (got %d)", d.d);
-  if (d.wtype == PI_W_F32 && d.rank > 0)
-    return fail(ctx, PI_ERR_UNSUPPORTED, "the predictor runs on fp16 tokens: fp32 layers take rank 0");
-  PI_TRY(check_dev_ptr(ctx, d.w_up, "w_up"));
-  PI_TRY(check_dev_ptr(ctx, d.w_down_t, "w_down_t"));
-  PI_TRY(check_dev_ptr(ctx, d.b, "b"));
-  if (d.act == PI_ACT_REGLU) PI_TRY(check_dev_ptr(ctx, d.w_gate, "w_gate"));
-  if (d.wtype == PI_W_Q4_0) {
-    PI_TRY(check_dev_ptr(ctx, d.s_up, "s_up"));
-    PI_TRY(check_dev_ptr(ctx, d.s_down, "s_down"));
-    if (d.act == PI_ACT_REGLU) PI_TRY(check_dev_ptr(ctx, d.s_gate, "s_gate"));
-  }
-  if (d.rank > 0) {
-    PI_TRY(check_dev_ptr(ctx, d.p_w1, "p_w1"));
-    PI_TRY(check_dev_ptr(ctx, d.p_w2, "p_w2"));
-    PI_TRY(check_dev_ptr(ctx, d.p_b, "p_b"));
-  }
+  PI_TRY(check_desc(ctx, d));
   pi_ffn* f = new (std::nothrow) pi_ffn();
   if (f == nullptr) return fail(ctx, PI_ERR_OOM, "host allocation failed");
   f->desc = d;
   f->ctx = ctx;
+  f->serial = g_ffn_serial.fetch_add(1);
   *out = f;
   return PI_OK;
 }
 
-void pi_ffn_destroy(pi_ffn* ffn) { delete ffn; }
+void pi_ffn_destroy(pi_ffn* ffn) {
+  if (ffn == nullptr) return;
+  // a captured stack step holding this layer's pointers is dropped with it
+  pi_ctx* c = ffn->ctx;
+  if (c != nullptr && std::find(c->g_layers.begin(), c->g_layers.end(), ffn->serial) != c->g_layers.end()) {
+    (void)hipSetDevice(c->device);
+    drop_graph(c);
+  }
+  delete ffn;
+}
 
 pi_status pi_predict(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, uint64_t* mask, int32_t* idx,
                      int32_t* n_active, float* logits_out) {
@@ -936,16 +994,17 @@ pi_status pi_compact(pi_ctx* ctx, const float* v, int32_t B, int32_t ffn, float 
   return launch_compact(ctx, ffn, idx, n_active);
 }
 
-pi_status pi_glue(pi_ctx* ctx, const float* y, const void* x_prev, int32_t B, int32_t d, int32_t x_is_f32,
-                  void* x_out) {
+pi_status pi_glue(pi_ctx* ctx, const float* y, const float* center, const void* x_prev, int32_t B, int32_t d,
+                  int32_t x_is_f32, void* x_out) {
   if (ctx == nullptr) return PI_ERR_INVALID;
   if (B < 1 || d < 8 || d % 8) return fail(ctx, PI_ERR_INVALID, "bad shape B=%d d=%d", B, d);
   PI_TRY(check_dev_ptr(ctx, y, "y"));
+  PI_TRY(check_dev_ptr(ctx, center, "center", true));
   PI_TRY(check_dev_ptr(ctx, x_prev, "x_prev"));
   PI_TRY(check_dev_ptr(ctx, x_out, "x_out"));
   PI_HIP(ctx, hipSetDevice(ctx->device));
-  if (x_is_f32) hipLaunchKernelGGL(k_glue<true>, dim3(B), dim3(BLOCK), 0, ctx->stream, y, x_prev, d, x_out);
-  else hipLaunchKernelGGL(k_glue<false>, dim3(B), dim3(BLOCK), 0, ctx->stream, y, x_prev, d, x_out);
+  if (x_is_f32) hipLaunchKernelGGL(k_glue<true>, dim3(B), dim3(BLOCK), 0, ctx->stream, y, center, x_prev, d, x_out);
+  else hipLaunchKernelGGL(k_glue<false>, dim3(B), dim3(BLOCK), 0, ctx->stream, y, center, x_prev, d, x_out);
   PI_HIP(ctx, hipGetLastError());
   return PI_OK;
 }
@@ -982,7 +1041,8 @@ pi_status pi_permute_rows(pi_ctx* ctx, const void* src, void* dst, const int32_t
 }
 
 static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens,
-                                   int32_t T, int32_t B, float* y_out, int32_t* n_active_log, int32_t use_graph) {
+                                   int32_t T, int32_t B, float* y_out, int32_t* n_active_log, int32_t use_graph,
+                                   const pi_stack_dump* dump) {
   if (layers == nullptr || L < 1) return fail(ctx, PI_ERR_INVALID, "need at least one layer");
   if (L > NLOG_CAP) return fail(ctx, PI_ERR_INVALID, "at most %d layers", NLOG_CAP);
   if (T < 1 || B < 1 || T % B) return fail(ctx, PI_ERR_INVALID, "T %d must be a positive multiple of B %d", T, B);
@@ -996,64 +1056,106 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
   PI_TRY(check_dev_ptr(ctx, x_tokens, "x_tokens"));
   PI_TRY(check_dev_ptr(ctx, y_out, "y_out"));
   PI_TRY(check_dev_ptr(ctx, n_active_log, "n_active_log", true));
+  if (dump != nullptr) {
+    PI_TRY(check_dev_ptr(ctx, dump->x, "dump.x", true));
+    PI_TRY(check_dev_ptr(ctx, dump->mask, "dump.mask", true));
+    PI_TRY(check_dev_ptr(ctx, dump->idx, "dump.idx", true));
+    PI_TRY(check_dev_ptr(ctx, dump->n, "dump.n", true));
+    PI_TRY(check_dev_ptr(ctx, dump->y, "dump.y", true));
+    if (dump->ffn_stride < 64 || dump->ffn_stride % 64)
+      return fail(ctx, PI_ERR_INVALID, "dump.ffn_stride %d must be a positive multiple of 64", dump->ffn_stride);
+    for (int l = 0; l < L; ++l)
+      if (layers[l]->desc.ffn > dump->ffn_stride)
+        return fail(ctx, PI_ERR_INVALID, "layer %d: ffn %d above dump.ffn_stride %d", l, layers[l]->desc.ffn,
+                    dump->ffn_stride);
+    use_graph = 0;
+  }
   PI_HIP(ctx, hipSetDevice(ctx->device));
   const int d = layers[0]->desc.d;
   const size_t xe = x_elem(layers[0]->desc.wtype);
   const size_t xbytes = (size_t)B * d * xe, ybytes = (size_t)B * d * 4;
+  // the chaining vector that feeds layer l: that of layer l - 1
+  auto center_into = [&](int l) -> const float* { return l > 0 ? layers[l - 1]->desc.y_center : nullptr; };
 
-  auto enqueue_step = [&]() -> pi_status {
+  // dump of step s after layer l: its input, its output (partial sums added) and, through the
+  // layer's own output arguments, its mask words, index list and count
+  auto dump_slot = [&](int s, int l) -> size_t { return (size_t)s * L + l; };
+  auto enqueue_step = [&](int s) -> pi_status {
     for (int l = 0; l < L; ++l) {
+      const size_t slot = dump != nullptr ? dump_slot(s, l) : 0;
+      uint64_t* mask_out = (dump != nullptr && dump->mask != nullptr)
+                               ? dump->mask + slot * (size_t)B * (dump->ffn_stride / 64) : nullptr;
+      int32_t* idx_out = (dump != nullptr && dump->idx != nullptr) ? dump->idx + slot * (size_t)dump->ffn_stride
+                                                                   : ctx->idx;
+      const void* x_cur;
       if (B > 8) {
         // batched layers take x from global memory: the glue runs as its own kernel
-        const void* x_in = ctx->xstage;
+        x_cur = ctx->xstage;
         if (l > 0) {
           const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
-          x_in = ctx->xbuf[l & 1];
+          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
+                               ctx->xbuf[l & 1]));
+          x_cur = ctx->xbuf[l & 1];
         }
-        PI_TRY(enqueue_batched(ctx, layers[l], x_in, B, ctx->y, nullptr, ctx->idx, ctx->nbuf, ctx->nlog + l));
-        continue;
-      }
-      XIn xin;
-      const void* x_cur;
-      if (l == 0) {
-        xin = XIn{ctx->xstage, nullptr, nullptr, 1, 0};
-        x_cur = ctx->xstage;
-      } else if (B > 1) {
-        // several tokens: every predictor workgroup would re-read B x d partial sums, so the
-        // partials are added and the glue applied once, by two small kernels
-        const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-        const int BD = B * d;
-        PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part, ctx->down_g,
-                             BD, ctx->y));
-        if (xe == 4)
-          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<true>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
-        else
-          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, x_prev, d, ctx->xbuf[l & 1]));
-        xin = XIn{ctx->xbuf[l & 1], nullptr, nullptr, 1, 0};
-        x_cur = ctx->xbuf[l & 1];
+        PI_TRY(enqueue_batched(ctx, layers[l], x_cur, B, ctx->y, mask_out, idx_out, ctx->nbuf, ctx->nlog + l));
       } else {
-        const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-        // the glue adds the previous layer's partial sums itself
-        xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], ctx->down_g, B * d};
-        x_cur = ctx->xbuf[l & 1];
+        XIn xin;
+        if (l == 0) {
+          xin = XIn{ctx->xstage, nullptr, nullptr, 1, 0, nullptr};
+          x_cur = ctx->xstage;
+        } else if (B > 1) {
+          // several tokens: every predictor workgroup would re-read B x d partial sums, so the
+          // partials are added and the glue applied once, by two small kernels
+          const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
+          const int BD = B * d;
+          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part, ctx->down_g,
+                               BD, ctx->y));
+          if (xe == 4)
+            PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<true>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
+                                 ctx->xbuf[l & 1]));
+          else
+            PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
+                                 ctx->xbuf[l & 1]));
+          xin = XIn{ctx->xbuf[l & 1], nullptr, nullptr, 1, 0, nullptr};
+          x_cur = ctx->xbuf[l & 1];
+        } else {
+          const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
+          // the glue adds the previous layer's partial sums itself
+          xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], ctx->down_g, B * d, center_into(l)};
+          x_cur = ctx->xbuf[l & 1];
+        }
+        PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, l == L - 1 ? ctx->y : nullptr, mask_out, idx_out,
+                             ctx->nbuf, ctx->nlog + l));
       }
-      PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, l == L - 1 ? ctx->y : nullptr, nullptr, ctx->idx,
-                           ctx->nbuf, ctx->nlog + l));
+      if (dump != nullptr) {
+        if (dump->x != nullptr)
+          PI_HIP(ctx, hipMemcpyAsync(static_cast<uint8_t*>(dump->x) + slot * xbytes, x_cur, xbytes,
+                                     hipMemcpyDeviceToDevice, ctx->stream));
+        if (dump->n != nullptr)
+          PI_HIP(ctx, hipMemcpyAsync(dump->n + slot, ctx->nbuf, 4, hipMemcpyDeviceToDevice, ctx->stream));
+        if (dump->y != nullptr) {
+          float* yd = dump->y + slot * (size_t)B * d;
+          if (B > 8 || l == L - 1) {
+            PI_HIP(ctx, hipMemcpyAsync(yd, ctx->y, ybytes, hipMemcpyDeviceToDevice, ctx->stream));
+          } else {
+            const int BD = B * d;
+            PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part, ctx->down_g,
+                                 BD, yd));
+          }
+        }
+      }
     }
     return PI_OK;
   };
 
   bool graph_ok = false;
   if (use_graph) {
-    std::vector<const pi_ffn*> key(layers, layers + L);
+    std::vector<uint64_t> key(L);
+    for (int l = 0; l < L; ++l) key[l] = layers[l]->serial;
     if (ctx->gexec != nullptr && ctx->g_layers == key && ctx->g_B == B) {
       graph_ok = true;
     } else {
-      if (ctx->gexec != nullptr) {
-        (void)hipGraphExecDestroy(ctx->gexec);
-        ctx->gexec = nullptr;
-      }
+      drop_graph(ctx);
       hipStream_t user = ctx->stream;
       ctx->stream = ctx->cap_stream;
       hipError_t e = hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal);
@@ -1061,7 +1163,7 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
         ctx->stream = user;
         return fail(ctx, PI_ERR_HIP, "graph capture: %s", hipGetErrorString(e));
       }
-      pi_status s = enqueue_step();
+      pi_status s = enqueue_step(0);
       hipGraph_t graph = nullptr;
       e = hipStreamEndCapture(ctx->cap_stream, &graph);
       ctx->stream = user;
@@ -1087,7 +1189,7 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
     if (graph_ok) {
       PI_HIP(ctx, hipGraphLaunch(ctx->gexec, ctx->stream));
     } else {
-      PI_TRY(enqueue_step());
+      PI_TRY(enqueue_step(s));
     }
     PI_HIP(ctx, hipMemcpyAsync(reinterpret_cast<uint8_t*>(y_out) + (size_t)s * ybytes, ctx->y, ybytes,
                                hipMemcpyDeviceToDevice, ctx->stream));
@@ -1101,7 +1203,14 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
 pi_status pi_stack_run(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens, int32_t T,
                        int32_t B, float* y_out, int32_t* n_active_log, int32_t use_graph) {
   if (ctx == nullptr) return PI_ERR_INVALID;
-  return pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, use_graph);
+  return pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, use_graph, nullptr);
+}
+
+pi_status pi_stack_run_dump(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens, int32_t T,
+                            int32_t B, float* y_out, int32_t* n_active_log, const pi_stack_dump* dump) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (dump == nullptr) return fail(ctx, PI_ERR_INVALID, "dump is NULL");
+  return pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, 0, dump);
 }
 
 pi_status pi_stack_profile(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, const void* x_tokens, int32_t T,
@@ -1111,7 +1220,7 @@ pi_status pi_stack_profile(pi_ctx* ctx, const pi_ffn* const* layers, int32_t L, 
   PI_HIP(ctx, hipSetDevice(ctx->device));
   ctx->profiling = true;
   ctx->ev_used = 0;
-  pi_status s = pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, 0);
+  pi_status s = pi_stack_run_impl(ctx, layers, L, x_tokens, T, B, y_out, n_active_log, 0, nullptr);
   ctx->profiling = false;
   if (s != PI_OK) return s;
   PI_HIP(ctx, hipStreamSynchronize(ctx->stream));

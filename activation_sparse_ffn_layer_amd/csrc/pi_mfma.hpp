@@ -49,6 +49,7 @@ struct MmRows {
                              // neurons (per-token masking). NULL: the union
   int lda;
   int ffn;
+  int hot_prefix;        // EPI_MASK: columns [0, hot_prefix) are taken without a prediction
 };
 
 // Whether token t keeps neuron i: always under the union; its own mask bit under per-token
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(BLOCK) void k_mm_gemm(MmRows p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * tb + mfma_row(r, lane);
-      const float v = acc[r] + bias;
+      const float v = (col < p.hot_prefix) ? __builtin_inff() : acc[r] + bias;  // hot prefix: +inf
       const bool bit = valid && t < p.B && v > p.threshold;
       any |= bit;
       const uint64_t bal = __ballot(bit);

@@ -3,10 +3,10 @@
 
 A step is one pass of the whole hot path over one batch: every layer of the stack runs the
 low-rank predictor, the threshold and compaction, the gathered up/gate rows with their
-activation and the scattered down columns, chained layer to layer by the rms glue. The
-default workload is the OPT-6.7B-shaped stack (32 ReLU layers, d=4096, ffn=16384, rank-1024
-fp16 predictor, fp16 weights) at batch 1, with seeded synthetic weights and tokens resident
-in HBM before timing starts.
+activation and the scattered down columns, chained layer to layer by the centred rms glue.
+The default workload is the largest: the OPT-175B-shaped stack (96 ReLU layers, d=12288,
+ffn=49152, Q4_0 weights, rank-1024 fp16 predictor) at batch 1, with seeded synthetic weights
+and tokens resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s over the timed steps, a roofline entry for the kernel that
 takes the most time (algorithmic bytes per launch over its HIP-event-timed duration, against
@@ -41,13 +41,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128, help="timed steps (one batch through the stack each)")
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--config", default="opt6.7b")
+    ap.add_argument("--config", default="opt175b")
     ap.add_argument("--batch", type=int, default=None, help="tokens per step (default: the workload's first batch)")
     ap.add_argument("--layers", type=int, default=None, help="override the stack depth (exploration only)")
     ap.add_argument("--act", choices=["relu", "reglu", "sqrelu"], default=None,
                     help="override the workload's activation family (e.g. the Squared-ReLU variant)")
     ap.add_argument("--mask", choices=["union", "per_token"], default="union",
                     help="masking of a batch: the union of the tokens' masks, or each token's own")
+    ap.add_argument("--hot-prefix", default="0",
+                    help="stored neurons of every layer taken without a prediction: a count, or 'auto' "
+                         "for the count the bytes model picks per layer (hot-first layouts)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-steps", type=int, default=16, help="steps of the per-kernel event pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -122,13 +125,35 @@ def calibrate_copy():
     log(f"copied {COPY_CAL_BYTES} bytes 3 times")
 
 
-def build_stack(cfg, seed, pi, ctx):
-    """Generate every layer in device memory; hot-first workloads are permuted on the device."""
+def hot_prefix_auto(L, B):
+    """Hot-prefix length that minimises a layer's expected bytes (hot-first layouts): a prefix
+    neuron saves its predictor row (2r bytes) but reads its up (gate) and down rows whether it
+    fires or not; a predicted neuron reads them with probability q_B = 1 - (1 - q)^B, q its
+    predicted-active probability Phi(mu / sqrt(1 + s2)). The prefix is the longest run from
+    the hottest neuron over which the cumulative saving keeps growing."""
+    import numpy as np
+    import scipy.special as sp
+    from synth import NOISE_VAR
+    if L.rank <= 0:
+        return 0
+    q = sp.ndtr(sp.ndtri(L.p) / math.sqrt(1.0 + NOISE_VAR))
+    qb = 1.0 - (1.0 - q) ** B
+    k = 3 if L.act == "reglu" else 2
+    rows = k * L.d * WBYTES[L.wtype]
+    gain = 2.0 * L.rank - (1.0 - qb) * rows          # per neuron, in stored (hot-first) order
+    c = np.cumsum(gain)
+    h = int(np.argmax(c)) + 1
+    return h if c[h - 1] > 0 else 0
+
+
+def build_stack(cfg, seed, pi, ctx, batch=1, mask_mode="union", hot_prefix="0"):
+    """Generate every layer in device memory; hot-first workloads are permuted on the device.
+    Each layer's chaining vector is computed for ``batch`` tokens per step under ``mask_mode``."""
     import torch
     from synth import make_layer
     layers, ffns, tables = [], [], []
     for li in range(cfg.layers):
-        L = make_layer(cfg, li, master=seed, device="cuda")
+        L = make_layer(cfg, li, master=seed, device="cuda", chain_batch=batch, chain_mode=mask_mode)
         table = None
         if cfg.hot_first:
             perm = torch.from_numpy(pi.hot_first_order(L.p)).cuda()
@@ -143,6 +168,9 @@ def build_stack(cfg, seed, pi, ctx):
                                     s_up=pr(L.s_up), s_gate=pr(L.s_gate), s_down=pr(L.s_down), b=pr(L.b),
                                     p_w2=pr(L.p_w2), p_b=pr(L.p_b), p=L.p[perm.cpu().numpy()])
             table = perm
+        if hot_prefix != "0" and L.rank > 0:
+            hp = hot_prefix_auto(L, batch) if hot_prefix == "auto" else min(int(hot_prefix), L.ffn)
+            L = dataclasses.replace(L, hot_prefix=hp)
         layers.append(L)
         tables.append(table)
         ffns.append(pi.Ffn(ctx, L, neuron_table=table))
@@ -174,7 +202,7 @@ def kernel_bytes(cls, L, B, n_list):
     if B > 8:
         if cls == "stage1":
             return len(n_list) * (r * d * 2 + B * d * 2 + B * r * 4)
-        if cls == "stage2":
+        if cls == "stage2":  # the matrix-core stage 2 reads every predictor row
             return len(n_list) * (F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8)
         if cls == "truemask":
             return len(n_list) * (F * d * 2 + F * 4 + B * d * 2 + (B + 1) * F / 8)
@@ -186,10 +214,11 @@ def kernel_bytes(cls, L, B, n_list):
     if cls == "stage1":
         return len(n_list) * (r * d * 2 + B * d * xe + B * r * 4)
     up_rows = lambda n: n * (k_up * d * w + 4 + 4 * B)  # noqa: E731  (rows, bias, a written)
+    Fp = F - getattr(L, "hot_prefix", 0)  # neurons with a prediction (predictor rows read)
     if cls == "stage2" and up_cols(L, B):  # predictor stage 2 + threshold only
-        return len(n_list) * (F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8)
+        return len(n_list) * (Fp * r * 2 + Fp * 4 + B * r * 4 + (B + 1) * F / 8)
     if cls == "stage2":  # predictor stage 2 + threshold + own active neurons' up (gate) rows
-        return sum(F * r * 2 + F * 4 + B * r * 4 + (B + 1) * F / 8 + B * d * xe + up_rows(n) for n in n_list)
+        return sum(Fp * r * 2 + Fp * 4 + B * r * 4 + (B + 1) * F / 8 + B * d * xe + up_rows(n) for n in n_list)
     if cls == "truemask":  # threshold GEMV + (ReGLU) own active neurons' up rows
         extra = (lambda n: up_rows(n)) if L.act == "reglu" else (lambda n: n * 4 * B)  # noqa: E731
         return sum(F * d * w + F * 4 + B * d * xe + (B + 1) * F / 8 + extra(n) for n in n_list)
@@ -216,6 +245,26 @@ def step_bytes(layers, B, nlog_rows):
     return total
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu), or /proc/cpuinfo's, or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.strip().startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, layers, x_tokens, B, budget_s, mask_mode="union"):
     """The fp64 oracle, as it stands, on a bounded sample: one batch of B tokens chained
     through the stack (union or per-token masking, like the GPU step) until the time budget
@@ -234,14 +283,15 @@ def cpu_baseline(cfg, layers, x_tokens, B, budget_s, mask_mode="union"):
         t0 = time.perf_counter()
         r = oracle.layer_forward(H, x)
         y = oracle.per_token_ffn(H, x, r["mask"]) if mask_mode == "per_token" else r["y"]
-        x = oracle.glue(y, x)
+        x = oracle.glue(y, x, H["glue_center"])
         elapsed += time.perf_counter() - t0
         done += 1
         del H
         if elapsed >= budget_s:
             break
     frac = done / len(layers)
-    return {"value": B * frac / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": B * frac / elapsed, "unit": "tokens/s", "cores": int(threads), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"one batch of {B} token(s) through {done} of the {len(layers)} layers "
                       f"({frac:.3f} of a step) in {elapsed:.1f} s of fp64 numpy compute, scaled to a whole "
                       f"step; weight copies to host not timed"}
@@ -272,7 +322,7 @@ def main():
     ctx.set_mask_mode(args.mask)
     log(f"generating {cfg.layers} layers of {cfg.name} on the GPU")
     t0 = time.perf_counter()
-    layers, ffns = build_stack(cfg, args.seed, pi, ctx)
+    layers, ffns = build_stack(cfg, args.seed, pi, ctx, batch=B, mask_mode=args.mask, hot_prefix=args.hot_prefix)
     log(f"  {sum(L.nbytes() for L in layers) / 1e9:.2f} GB of weights in {time.perf_counter() - t0:.1f} s")
     T_w, T = args.warmup * B, args.steps * B
     X = make_tokens(cfg, T_w + T, master=args.seed, device="cuda", stream=12345)
@@ -350,7 +400,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}-shaped {cfg.act} FFN stack, batch {B}", "layers": cfg.layers, "d": cfg.d,
                    "ffn": cfg.ffn, "rank": cfg.rank, "weights": cfg.wtype, "batch": B, "seed": args.seed,
-                   "hot_first": cfg.hot_first, "graph": use_graph, "mask": args.mask},
+                   "hot_first": cfg.hot_first, "graph": use_graph, "mask": args.mask,
+                   "hot_prefix": int(sum(getattr(L, "hot_prefix", 0) for L in layers))},
         "hbm_frac_active": round(frac_active, 4),
         "stream_read_gbs": round(stream_gbs, 1),
         "frac_of_stream_read": round(active_bytes / elapsed_s / 1e9 / stream_gbs, 4),

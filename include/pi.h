@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 1
+#define PI_ABI_VERSION 2
 
 typedef enum {
   PI_OK = 0,
@@ -76,7 +76,15 @@ typedef struct pi_ffn pi_ffn;
  *   p_w1     fp16 [rank][d], p_w2 fp16 [ffn][rank], p_b fp32 [ffn]: the low-rank predictor
  *            logit = p_w2 (p_w1 x) + p_b (P3 «Prediktor Kepadatan Adaptif»); NULL if rank 0
  *   neuron_table  int32 [ffn] stored row -> original neuron id, or NULL (identity).
- *            Informational: outputs are in stored order. */
+ *            Informational: outputs are in stored order.
+ *   hot_prefix  H in [0, ffn]: the first H stored neurons are taken for every token without
+ *            a prediction (their predictor rows are not read, their decision value is +inf)
+ *            and the activation itself zeroes those that do not fire: the hot neurons
+ *            PowerInfer keeps resident and always computes (P1 header bullets and «CPU/GPU
+ *            hibrit çıkarım yöntemi»; P3 «Penempatan dan Pengelolaan Neuron»), on a hot-first
+ *            layout. Predictor layers only (rank > 0); 0 for none.
+ *   y_center fp32 [d] or NULL: this layer's expected output, subtracted from its y before the
+ *            normalisation that feeds the next layer of a stack (pi_stack_run, pi_glue). */
 typedef struct pi_ffn_desc {
   int32_t d, ffn, rank;
   int32_t act;
@@ -88,6 +96,8 @@ typedef struct pi_ffn_desc {
   const uint16_t *p_w1, *p_w2;
   const float *p_b;
   const int32_t *neuron_table;
+  int32_t hot_prefix;
+  const float *y_center;
 } pi_ffn_desc;
 
 int32_t pi_abi_version(void);
@@ -149,31 +159,66 @@ pi_status pi_predict(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, u
 pi_status pi_sparse_ffn(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B,
                         const int32_t *idx, const int32_t *n_active, float *y);
 
-/* pi_predict followed by pi_sparse_ffn on its union list. mask, idx and n_active are
- * nullable outputs (context scratch is used when NULL). */
+/* One FFN layer for B tokens (P3 «Fase Online»: the predictor marks the neurons likely to
+ * fire, inactive ones are skipped, active ones computed): pi_predict followed by
+ * pi_sparse_ffn on its union list, as three or four fused kernels. mask, idx and n_active
+ * are nullable outputs (context scratch is used when NULL). */
 pi_status pi_layer(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, float *y,
                    uint64_t *mask, int32_t *idx, int32_t *n_active);
 
 /* Threshold + compaction alone, on caller-provided decision values v [B][ffn] fp32:
- * the same device code pi_predict uses after computing v. */
+ * the same device code pi_predict uses after computing v (P3 «Prediktor Kepadatan Adaptif»:
+ * neurons predicted active are processed; P3 «Operator yang Sadar Neuron»: they are then
+ * addressed directly, with no dense conversion). B is 1..8. */
 pi_status pi_compact(pi_ctx *ctx, const float *v, int32_t B, int32_t ffn, float threshold,
                      uint64_t *mask, int32_t *idx, int32_t *n_active);
 
-/* Chain between stacked layers: x_out_t = round(y_t / sqrt(mean(y_t^2))) to x's storage
- * type (fp16, or fp32 when x_is_f32), or x_prev_t unchanged when y_t is all zero.
- *   y [B][d] fp32, x_prev [B][d], x_out [B][d] */
-pi_status pi_glue(pi_ctx *ctx, const float *y, const void *x_prev, int32_t B, int32_t d,
-                  int32_t x_is_f32, void *x_out);
+/* Chain between stacked layers, so that each token passes through every layer before the
+ * next token (P3 introduction). The pages define no layer between FFNs; this one keeps every
+ * layer's input at the scale its calibration assumes: u_t = y_t - c, x_out_t = round(u_t /
+ * sqrt(mean(u_t^2))) to x's storage type (fp16, or fp32 when x_is_f32), or x_prev_t
+ * unchanged when y_t (or u_t) is all zero.
+ *   y [B][d] fp32, center c fp32 [d] or NULL (zero), x_prev [B][d], x_out [B][d] */
+pi_status pi_glue(pi_ctx *ctx, const float *y, const float *center, const void *x_prev, int32_t B,
+                  int32_t d, int32_t x_is_f32, void *x_out);
 
 /* Run L layers over T tokens, B tokens per step (T % B == 0), one step at a time: step s
- * feeds x_tokens[s*B..s*B+B) to layer 0, each layer's y (through pi_glue) to the next, and
- * writes the last layer's y to y_out[s*B..]. Token-by-token decode (P3 intro) at B == 1.
+ * feeds x_tokens[s*B..s*B+B) to layer 0, each layer's y (through pi_glue, with that layer's
+ * y_center) to the next, and writes the last layer's y to y_out[s*B..]. Token-by-token
+ * decode (P3 intro) at B == 1.
  *   layers     host array of L layer handles with equal d and activation/weight types
  *   x_tokens   [T][d] fp16 (fp32 for PI_W_F32 stacks); y_out [T][d] fp32
  *   n_active_log nullable device int32 [T/B][L]: n_active of every (step, layer)
  *   use_graph  nonzero: each step's L layers run as one captured HIP graph */
 pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, const void *x_tokens,
                        int32_t T, int32_t B, float *y_out, int32_t *n_active_log, int32_t use_graph);
+
+/* What pi_stack_run_dump records of every (step, layer); each pointer is DEVICE memory or
+ * NULL (not recorded). With S = T/B steps, slot (s, l) is at index s*L + l:
+ *   x     [S][L][B][d] in x's storage type: the layer's input as its kernels read it
+ *   mask  [S][L][B][ffn_stride/64] uint64: the tokens' predicted mask words
+ *   idx   [S][L][ffn_stride] int32: the ascending union list (entries past n unspecified)
+ *   n     [S][L] int32: the union count
+ *   y     [S][L][B][d] fp32: the layer's output (its partial sums added)
+ *   ffn_stride  >= every layer's ffn, a multiple of 64 */
+typedef struct pi_stack_dump {
+  void *x;
+  uint64_t *mask;
+  int32_t *idx;
+  int32_t *n;
+  float *y;
+  int32_t ffn_stride;
+} pi_stack_dump;
+
+/* pi_stack_run with every layer's input, mask, index list, count and output recorded, for
+ * checking a whole stack layer by layer against a reference that takes each layer's
+ * recorded input (P3 «Fase Online»: per layer, predict, skip the inactive, compute the
+ * active). Runs the same kernels in the same order as pi_stack_run, eagerly (no graph),
+ * with copies and sums of partials into the dump between layers; y_out and n_active_log are
+ * therefore bitwise those of pi_stack_run. Other arguments as for pi_stack_run. */
+pi_status pi_stack_run_dump(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, const void *x_tokens,
+                            int32_t T, int32_t B, float *y_out, int32_t *n_active_log,
+                            const pi_stack_dump *dump);
 
 /* Kernel classes of pi_stack_profile's outputs, in this order:
  * predictor stage 1 (with the glue); predictor stage 2 + threshold + the activations of the
@@ -188,10 +233,11 @@ pi_status pi_stack_run(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, cons
 
 /* pi_stack_run without a graph, every kernel dispatched with a pair of hipEvents
  * (hipExtLaunchKernelGGL) on the context's stream, so each pair times that kernel's own
- * execution. Blocks until the work is done, then writes the summed event time in
- * milliseconds (ms_out[PI_KERNEL_CLASSES], host) and the number of launches
- * (launches_out[PI_KERNEL_CLASSES], host) of each kernel class. Other arguments as for
- * pi_stack_run. For measurement. */
+ * execution: the per-kernel time of the generation speed the pages measure end to end
+ * in tokens/s (P1 «Performans değerlendirmesi ve demo»). Blocks until the work is done,
+ * then writes the summed event time in milliseconds (ms_out[PI_KERNEL_CLASSES], host) and
+ * the number of launches (launches_out[PI_KERNEL_CLASSES], host) of each kernel class.
+ * Other arguments as for pi_stack_run. For measurement. */
 pi_status pi_stack_profile(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, const void *x_tokens,
                            int32_t T, int32_t B, float *y_out, int32_t *n_active_log, double *ms_out,
                            int64_t *launches_out);
@@ -202,7 +248,9 @@ pi_status pi_stack_profile(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, 
 pi_status pi_hot_first_order(const double *p, int32_t ffn, int32_t *perm);
 
 /* Gather rows on the device: dst[k] = src[perm[k]] for k < rows, each row_bytes long
- * (a multiple of 4). Used to store a layer's neuron-indexed arrays in hot-first order.
+ * (a multiple of 4). Used to store a layer's neuron-indexed arrays in hot-first order
+ * (P3 «Penempatan dan Pengelolaan Neuron»: neurons placed by hotness, with a table back to
+ * their original positions).
  * perm is a device int32 [rows] permutation; src and dst must not overlap. */
 pi_status pi_permute_rows(pi_ctx *ctx, const void *src, void *dst, const int32_t *perm,
                           int32_t rows, int64_t row_bytes);

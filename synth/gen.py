@@ -136,33 +136,35 @@ def expected_top_share(p: np.ndarray, top_fraction: float) -> float:
     return float(mass[:k].sum() / mass.sum())
 
 
-def chain_activation(b: np.ndarray, sh: np.ndarray, sn: Optional[np.ndarray], act: str, batch: int,
-                     mode: str = "union", points: int = 801) -> np.ndarray:
+def chain_activation(b, sh, sn, act: str, batch: int, mode: str = "union", points: int = 801) -> torch.Tensor:
     """E[a_i] of each neuron for x ~ N(0, I) (input-side calibration of the chaining vector).
 
     ``h ~ N(b, sh^2)``; ``sn`` the predictor noise std (None: no predictor, mask h > 0).
     Under the union of a batch of ``batch`` tokens a neuron a token does not predict itself
-    still counts when another token predicts it. Quadrature over h on +-8 sh."""
+    still counts when another token predicts it. Quadrature over h on +-8 sh, in float64 on
+    the device of ``sh`` (torch tensors or arrays)."""
+    sh = torch.as_tensor(sh, dtype=torch.float64)
+    dev = sh.device
+    b = torch.as_tensor(b, dtype=torch.float64, device=dev)
     if act == "reglu":
-        return np.zeros_like(b, dtype=np.float64)
-    g = np.linspace(-8.0, 8.0, points)
-    wq = np.exp(-0.5 * g * g) / math.sqrt(2.0 * math.pi) * (g[1] - g[0])
-    b = np.asarray(b, dtype=np.float64)[:, None]
-    sh = np.asarray(sh, dtype=np.float64)[:, None]
-    h = b + sh * g[None, :]
-    f = np.maximum(h, 0.0)
+        return torch.zeros_like(b)
+    g = torch.linspace(-8.0, 8.0, points, dtype=torch.float64, device=dev)
+    wq = torch.exp(-0.5 * g * g) / math.sqrt(2.0 * math.pi) * (g[1] - g[0])
+    h = b[:, None] + sh[:, None] * g[None, :]
+    f = torch.clamp_min(h, 0.0)
     if act == "sqrelu":
         f = f * f
     elif act != "relu":
         raise ValueError(act)
     if sn is None:
-        return (f * wq).sum(axis=1)
-    pv = sp.ndtr(h / np.asarray(sn, dtype=np.float64)[:, None])     # P(logit > 0 | h)
-    own = (f * pv * wq).sum(axis=1)
+        return (f * wq).sum(dim=1)
+    sn = torch.as_tensor(sn, dtype=torch.float64, device=dev)
+    pv = torch.special.ndtr(h / sn[:, None])                      # P(logit > 0 | h)
+    own = (f * pv * wq).sum(dim=1)
     if mode == "per_token" or batch <= 1:
         return own
-    other = (f * (1.0 - pv) * wq).sum(axis=1)
-    q = (pv * wq).sum(axis=1)
+    other = (f * (1.0 - pv) * wq).sum(dim=1)
+    q = (pv * wq).sum(dim=1)
     return own + other * (1.0 - (1.0 - q) ** (batch - 1))
 
 
@@ -351,21 +353,20 @@ def make_layer(cfg: StackConfig, layer: int, master: int = 0, device="cpu", chai
     glue_center = None
     if chain:
         # spreads of the stored masked rows' pre-activation and of the predictor's noise
-        sig_h = torch.sqrt((m_val * m_val).sum(dim=1)).double().cpu().numpy()
+        sig_h = torch.sqrt((m_val * m_val).sum(dim=1))
         sig_n = None
         if r > 0:
             w1f = p_w1.to(torch.float32)
-            sn = torch.empty(ffn, dtype=torch.float32, device=device)
+            sig_n = torch.empty(ffn, dtype=torch.float32, device=device)
             for r0 in range(0, ffn, 4096):
                 nr = p_w2[r0:r0 + 4096].to(torch.float32) @ w1f - m_val[r0:r0 + 4096]
-                sn[r0:r0 + 4096] = torch.sqrt((nr * nr).sum(dim=1))
+                sig_n[r0:r0 + 4096] = torch.sqrt((nr * nr).sum(dim=1))
                 del nr
-            sig_n = sn.double().cpu().numpy()
-            del w1f, sn
-        ea = chain_activation(sp.ndtri(p), sig_h, sig_n, cfg.act, chain_batch, chain_mode)
-        ea = torch.from_numpy(ea.astype(np.float32)).to(device)
+            del w1f
+        ea = chain_activation(torch.from_numpy(sp.ndtri(p)).to(device), sig_h, sig_n, cfg.act, chain_batch,
+                              chain_mode).to(torch.float32)
         glue_center = (ea.unsqueeze(0) @ dn_val).squeeze(0).contiguous()
-        del ea
+        del ea, sig_h, sig_n
     del m_val, dn_val
     if cfg.act in ("relu", "sqrelu"):
         up, s_up, gate, s_gate = m_w, m_s, None, None

@@ -59,10 +59,14 @@ def run_layer(ctx, ffn: "pi.Ffn", x: torch.Tensor, with_logits=False):
     return out
 
 
-def check_layer(host: dict, x_host: np.ndarray, out: dict, tol: float, check_logits=False):
-    """Assert parity of one batch; returns (#band neurons, #band neurons decided differently)."""
+def check_layer(host: dict, x_host: np.ndarray, out: dict, tol: float, check_logits=False, v=None, ref=None):
+    """Assert parity of one batch; returns (#band neurons, #band neurons decided differently).
+
+    ``v``: the oracle's decision values of x_host when already computed. ``ref``: a dict that
+    receives the expected y (``ref["y"]``, [B][d] float64)."""
     ffn = host["ffn"]
-    v = oracle.decision_values(host, x_host)
+    if v is None:
+        v = oracle.decision_values(host, x_host)
     m_or = oracle.threshold(v, host["threshold"])
     band = oracle.band(v, host["threshold"])
     m_gpu = words_to_bool(out["mask"], ffn)
@@ -77,7 +81,10 @@ def check_layer(host: dict, x_host: np.ndarray, out: dict, tol: float, check_log
     np.testing.assert_array_equal(out["idx"][:n].cpu().numpy(), oracle.compact(u_gpu))
     if check_logits:
         lg = out["logits"].cpu().numpy().astype(np.float64)
-        assert np.max(np.abs(lg - v)) < oracle.THRESHOLD_BAND, np.max(np.abs(lg - v))
+        fin = np.isfinite(v)                       # hot-prefix neurons: +inf on both sides
+        np.testing.assert_array_equal(lg[~fin], v[~fin])
+        if fin.any():
+            assert np.max(np.abs(lg[fin] - v[fin])) < oracle.THRESHOLD_BAND, np.max(np.abs(lg[fin] - v[fin]))
         np.testing.assert_array_equal(words_to_bool(out["mask_p"], ffn), m_gpu)
         assert int(out["n_p"].item()) == n
         np.testing.assert_array_equal(out["idx_p"][:n].cpu().numpy(), out["idx"][:n].cpu().numpy())
@@ -96,7 +103,38 @@ def check_layer(host: dict, x_host: np.ndarray, out: dict, tol: float, check_log
         else:
             e = rel_l2(y[t], y_ref[t])
             assert e <= tol, f"token {t}: rel L2 {e:.3e} > {tol}"
+    if ref is not None:
+        ref["y"] = y_ref
     return int(band.sum()), int(np.sum(diff))
+
+
+def check_dump_layer(host: dict, dump: dict, layer: int, tol: float, next_x=None):
+    """Teacher-forced parity of one layer of a recorded stack (pi_stack_run_dump): for every
+    step, the oracle takes the layer's recorded input and the recorded mask words, index
+    list, count and y are checked as in :func:`check_layer`. With ``next_x`` (the next layer's
+    recorded inputs [S][B][d]), the chaining is checked too: the next input is within
+    2 * tol + 1e-3 (relative L2 per token) of the oracle's glue of the oracle's y (the
+    layer's expected output subtracted). Host arrays in ``dump``: x [S][L][B][d], mask
+    [S][L][B][W], idx [S][L][stride], n [S][L], y [S][L][B][d]. Returns (band, flips)."""
+    xs = dump["x"][:, layer]
+    S, B, d = xs.shape
+    W = host["ffn"] // 64
+    v_all = oracle.decision_values(host, xs.reshape(S * B, d)).reshape(S, B, -1)
+    bands = flips = 0
+    for s in range(S):
+        out = {"mask": torch.from_numpy(np.ascontiguousarray(dump["mask"][s, layer, :, :W])),
+               "idx": torch.from_numpy(dump["idx"][s, layer]), "n": torch.tensor([int(dump["n"][s, layer])]),
+               "y": torch.from_numpy(dump["y"][s, layer])}
+        ref = {}
+        nb, nf = check_layer(host, xs[s], out, tol, v=v_all[s], ref=ref)
+        bands += nb
+        flips += nf
+        if next_x is not None:
+            want = oracle.glue(ref["y"], xs[s], host.get("glue_center"))
+            for t in range(B):
+                e = rel_l2(next_x[s, t].astype(np.float64), want[t].astype(np.float64))
+                assert e <= 2 * tol + 1e-3, f"step {s} token {t}: next input off by rel L2 {e:.3e}"
+    return bands, flips
 
 
 def check_layer_per_token(host: dict, x_host: np.ndarray, out: dict, tol: float):

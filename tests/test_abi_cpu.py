@@ -29,9 +29,25 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib._SIGS), "binding and header disagree"
 
 
+COMPUTE_CALLS = ("pi_predict", "pi_sparse_ffn", "pi_layer", "pi_compact", "pi_glue", "pi_stack_run",
+                 "pi_stack_run_dump", "pi_stack_profile", "pi_hot_first_order", "pi_permute_rows")
+
+
+def test_every_compute_call_cites_the_pages():
+    """The comment right above each compute call's declaration names the passage of the pages
+    that defines the operation (P1/P2/P3 with a section in «», or a page's introduction or
+    header bullets)."""
+    text = open(HEADER).read()
+    cite = re.compile(r"P[123] (?:«[^»]+»|intro|header)")
+    for name in COMPUTE_CALLS:
+        m = re.search(r"(/\*(?:(?!\*/).)*\*/)\s*pi_status\s+" + name + r"\s*\(", text, flags=re.S)
+        assert m, f"{name}: no comment directly above its declaration"
+        assert cite.search(m.group(1)), f"{name}: its comment cites no passage of the pages"
+
+
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.pi_abi_version() == 1
+    assert L.pi_abi_version() == 2
     assert L.pi_status_str(0) == b"ok"
     assert L.pi_status_str(1) == b"invalid argument"
     assert L.pi_last_error(None) == b""

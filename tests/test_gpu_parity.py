@@ -119,6 +119,12 @@ CASES = {
     "reglu-b64-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 2, 64, 64),
     "reglu-b40-truemask-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 3, 40, 40),
     "llama-full-b64-mfma": (_cfg("llama70b"), 1, 64, 64),
+    # batch sizes between the classes: 6 and 7 tokens on the 8-token vector kernels, 12 on the
+    # matrix cores
+    "f16-b6": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 12, 6),
+    "q4-b7": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 3, 14, 7),
+    "relu-b12-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 3, 24, 12),
+    "reglu-b7-cols": (_cfg("llama70b", d=8192, ffn=4096, rank=512), 1, 7, 7),
 }
 
 
@@ -139,6 +145,37 @@ def test_layer_parity(case):
         bands += nb
         flips += nf
     _say(f"  {case}: band neurons {bands}, decided differently {flips}")
+
+
+# hot prefix: the first H stored neurons are taken without a prediction (H not a multiple of
+# 8 leaves a mask byte half predicted; H = ffn is the dense FFN)
+HP_CASES = {
+    "hp-f16-b1": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 0, 4, 1, 300),
+    "hp-f16-b1-ragged": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 1, 4, 1, 101),
+    "hp-q4-b1-cols": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 0, 4, 1, 517),
+    "hp-f16-b4": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 8, 4, 256),
+    "hp-reglu-b2": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 0, 4, 2, 77),
+    "hp-relu-b16-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 32, 16, 333),
+    "hp-all-b1": (_cfg("opt6.7b", d=1024, ffn=2048, rank=512), 0, 2, 1, 2048),
+}
+
+
+@pytest.mark.parametrize("case", list(HP_CASES))
+def test_layer_parity_hot_prefix(case):
+    cfg, li, T, B, hp = HP_CASES[case]
+    _say(f"hot-prefix parity {case}: d={cfg.d} ffn={cfg.ffn} rank={cfg.rank} {cfg.wtype} {cfg.act} B={B} H={hp}")
+    L = dataclasses.replace(make_layer(cfg, li, device="cuda"), hot_prefix=hp)
+    H = L.to_host()
+    X = make_tokens(cfg, T, device="cuda", stream=li + 3)
+    ctx = make_ctx([L], max_batch=max(8, B))
+    ffn = pi.Ffn(ctx, L)
+    for s in range(T // B):
+        x = X[s * B:(s + 1) * B].contiguous()
+        out = run_layer(ctx, ffn, x, with_logits=True)
+        check_layer(H, x.cpu().numpy(), out, TOL[cfg.wtype], check_logits=True)
+        m = words_to_bool(out["mask"], cfg.ffn)
+        assert m[:, :hp].all(), "a hot-prefix neuron is missing from a token's mask"
+        assert bool(torch.all(out["logits"][:, :hp] == float("inf")))
 
 
 # per-token masking: each token gets only its own predicted neurons (vector and matrix paths)
@@ -318,19 +355,27 @@ def test_sparse_ffn_column_slices_on_oracle_index_list(act):
 # ------------------------------------------------------------------------------- glue
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
-def test_glue(dtype):
+@pytest.mark.parametrize("centered", [False, True])
+def test_glue(dtype, centered):
     rng = np.random.default_rng(11)
-    B, d = 3, 4096
+    B, d = 4, 4096
+    c = rng.normal(0, 1.5, d).astype(np.float32) if centered else None
     y = rng.normal(0, 2.5, (B, d)).astype(np.float32)
     y[1] = 0
+    if centered:
+        y[3] = c + rng.normal(0, 0.5, d).astype(np.float32)   # mostly the common component
+        y[2] = c                                              # nothing but it: x passes through
     xp = rng.normal(0, 1, (B, d)).astype(np.float16 if dtype == torch.float16 else np.float32)
     ctx = pi.Context(max_batch=4, max_d=d, max_ffn=64, max_rank=0)
     xo = torch.empty((B, d), dtype=dtype, device="cuda")
-    pi.glue(ctx, torch.from_numpy(y).cuda(), torch.from_numpy(xp).cuda(), xo)
+    pi.glue(ctx, torch.from_numpy(y).cuda(), torch.from_numpy(xp).cuda(), xo,
+            None if c is None else torch.from_numpy(c).cuda())
     torch.cuda.synchronize()
-    ref = oracle.glue(y.astype(np.float64), xp)
+    ref = oracle.glue(y.astype(np.float64), xp, None if c is None else c.astype(np.float64))
     got = xo.cpu().numpy()
     np.testing.assert_array_equal(got[1], xp[1])
+    if centered:
+        np.testing.assert_array_equal(got[2], xp[2])
     if dtype == torch.float16:
         # fp32 arithmetic then one rounding to fp16: at most one fp16 ulp from the fp64 result
         ulp = np.spacing(np.abs(ref.astype(np.float16))).astype(np.float64)
@@ -402,7 +447,7 @@ def test_stack_glue_of_partials_equals_layer_by_layer(d, B):
             out = run_layer(ctx, f, x)
             if li + 1 < len(ffns):
                 xn = torch.empty_like(x)
-                pi.glue(ctx, out["y"], x, xn)
+                pi.glue(ctx, out["y"], x, xn, layers[li].glue_center)
                 x = xn
         torch.cuda.synchronize()
         for t in range(B):
@@ -433,6 +478,29 @@ def test_stack_glue_passes_x_through_an_all_zero_layer(B):
         out = run_layer(ctx, ffns[1], X[s * B:(s + 1) * B].contiguous())
         torch.cuda.synchronize()
         assert torch.equal(y_stack[s * B:(s + 1) * B], out["y"]), f"step {s}"
+
+
+def test_stack_graph_follows_rebuilt_layers():
+    """A stack step captured as a graph holds its layers' weight pointers. Destroying the
+    layers and wrapping other weights (on handles the allocator may place at the same
+    addresses) must not replay the old graph: the graph run equals the eager run."""
+    cfg = _cfg("opt6.7b", layers=2, d=1024, ffn=2048, rank=512)
+    X = make_tokens(cfg, 2, device="cuda")
+    ctx = make_ctx([make_layer(cfg, 0, device="cuda")], max_batch=1)
+    ys = []
+    for seed in (0, 1):
+        layers = [make_layer(cfg, i, master=seed, device="cuda") for i in range(cfg.layers)]
+        ffns = [pi.Ffn(ctx, L) for L in layers]
+        yg = torch.empty((2, cfg.d), dtype=torch.float32, device="cuda")
+        ye = torch.empty_like(yg)
+        pi.stack_run(ctx, ffns, X, 1, yg, None, use_graph=True)
+        pi.stack_run(ctx, ffns, X, 1, ye, None, use_graph=False)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye), f"seed {seed}: graph and eager runs differ"
+        ys.append(yg)
+        for f in ffns:
+            f.close()
+    assert not torch.equal(ys[0], ys[1])
 
 
 # ------------------------------------------------------------------------ permutation
