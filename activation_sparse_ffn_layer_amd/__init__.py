@@ -16,7 +16,7 @@ import torch
 
 from ._lib import ACT, KERNEL_CLASSES, MASK_MODE, PI_OK, WTYPE, FfnDesc, PiError, StackDump, _ptr, lib
 
-__all__ = ["Context", "Ffn", "PiError", "predict", "sparse_ffn", "layer", "compact", "glue", "stack_run",
+__all__ = ["Context", "Ffn", "PiError", "predict", "sparse_ffn", "layer", "layer_noalloc", "compact", "glue", "stack_run",
            "stack_run_dump", "stack_profile", "KERNEL_CLASSES",
            "hot_first_order", "permute_rows", "lib"]
 
@@ -111,6 +111,19 @@ def layer(ctx: Context, ffn: Ffn, x: torch.Tensor, y: torch.Tensor, mask: Option
           idx: Optional[torch.Tensor] = None, n_active: Optional[torch.Tensor] = None):
     ctx.check(lib().pi_layer(ctx.handle, ffn.handle, _ptr(x), x.shape[0], _ptr(y), _ptr(mask), _ptr(idx),
                              _ptr(n_active)))
+
+
+def layer_noalloc(layer, x: torch.Tensor, y: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                  idx: Optional[torch.Tensor] = None, n_active: Optional[torch.Tensor] = None,
+                  device: int = 0, stream: Optional[torch.cuda.Stream] = None):
+    """pi_layer_noalloc: one layer with no context and no device allocation (the library's fixed
+    scratch array). Raises PiError with the status on failure."""
+    st = stream if stream is not None else torch.cuda.current_stream(device)
+    desc = _desc(layer)
+    status = lib().pi_layer_noalloc(device, c_void_p(st.cuda_stream), ctypes.byref(desc), _ptr(x), x.shape[0],
+                                    _ptr(y), _ptr(mask), _ptr(idx), _ptr(n_active))
+    if status != PI_OK:
+        raise PiError(status, "pi_layer_noalloc failed")
 
 
 def compact(ctx: Context, v: torch.Tensor, threshold: float, mask: torch.Tensor, idx: torch.Tensor,

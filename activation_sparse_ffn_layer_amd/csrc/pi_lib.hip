@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -794,6 +795,50 @@ pi_status enqueue_layer(pi_ctx* c, const pi_ffn* f, const XIn& xin, const void* 
   return launch_down<true>(c, L, B, nullptr, nullptr, y, idx, n, n_log, per_tok ? mask : nullptr);
 }
 
+// ---------------------------------------------------------------- allocation-free layer
+
+// Scratch of pi_layer_noalloc: one fixed device array, which every GPU the library runs on
+// holds (at its own address) until the process ends. Sized for batches up to NOALLOC_B
+// tokens and layers up to NOALLOC_D x NOALLOC_F with rank up to NOALLOC_R, laid out like a
+// context's scratch without the stack runner's buffers.
+constexpr int NOALLOC_B = 8, NOALLOC_D = 12288, NOALLOC_F = 49152, NOALLOC_R = 1024;
+constexpr int NOALLOC_DEVICES = 64;
+constexpr WsLayout NOALLOC_LAYOUT = ws_layout(NOALLOC_B, NOALLOC_D, NOALLOC_F, NOALLOC_R, false);
+static_assert(NOALLOC_LAYOUT.total <= (size_t)32 << 20, "the fixed scratch stays modest");
+
+__device__ __align__(256) uint8_t scratch[NOALLOC_LAYOUT.total];
+
+// Per device: the array's device address (from hipGetSymbolAddress with that device current;
+// the symbol's host-side name is not a device address) and the limits the launches need.
+struct NoallocDev {
+  void* ptr = nullptr;
+  int cus = 256;
+  size_t lds_max = 65536;
+};
+std::mutex g_noalloc_mu;
+NoallocDev g_noalloc[NOALLOC_DEVICES];
+
+pi_status noalloc_device(int device, NoallocDev* out) {
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoallocDev& dv = g_noalloc[device];
+  if (dv.ptr == nullptr) {
+    if (hipSetDevice(device) != hipSuccess) return PI_ERR_HIP;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return PI_ERR_HIP;
+    }
+    int cus = 0, lds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cus > 0)
+      dv.cus = cus;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device) == hipSuccess && lds > 0)
+      dv.lds_max = (size_t)lds;
+    dv.ptr = ptr;
+  }
+  *out = dv;
+  return PI_OK;
+}
+
 }  // namespace
 
 // ======================================================================== exported ABI
@@ -969,6 +1014,37 @@ pi_status pi_layer(pi_ctx* ctx, const pi_ffn* ffn, const void* x, int32_t B, flo
     return enqueue_batched(ctx, ffn, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
   const XIn xin{x, nullptr, nullptr, 1, 0};
   return enqueue_layer(ctx, ffn, xin, x, B, y, mask, idx ? idx : ctx->idx, n_active ? n_active : ctx->nbuf, nullptr);
+}
+
+pi_status pi_layer_noalloc(int32_t device, void* hip_stream, const pi_ffn_desc* desc, const void* x, int32_t B,
+                           float* y, uint64_t* mask, int32_t* idx, int32_t* n_active) {
+  if (desc == nullptr || device < 0 || device >= NOALLOC_DEVICES || B < 1) return PI_ERR_INVALID;
+  if (B > NOALLOC_B || desc->d > NOALLOC_D || desc->ffn > NOALLOC_F || desc->rank > NOALLOC_R)
+    return PI_ERR_UNSUPPORTED;
+  NoallocDev dv;
+  PI_TRY(noalloc_device(device, &dv));
+  // a host-side context over the device's fixed scratch: nothing is allocated on the device
+  pi_ctx c;
+  c.device = device;
+  c.stream = static_cast<hipStream_t>(hip_stream);
+  c.max_batch = NOALLOC_B;
+  c.max_d = NOALLOC_D;
+  c.max_ffn = NOALLOC_F;
+  c.max_rank = NOALLOC_R;
+  c.cus = dv.cus;
+  c.lds_max = dv.lds_max;
+  ws_assign(&c, static_cast<uint8_t*>(dv.ptr), NOALLOC_LAYOUT);
+  PI_TRY(check_desc(&c, *desc));
+  PI_TRY(check_batch(&c, *desc, B));
+  PI_TRY(check_dev_ptr(&c, x, "x"));
+  PI_TRY(check_dev_ptr(&c, y, "y"));
+  PI_TRY(check_dev_ptr(&c, mask, "mask", true));
+  PI_TRY(check_dev_ptr(&c, idx, "idx", true));
+  PI_TRY(check_dev_ptr(&c, n_active, "n_active", true));
+  if (hipSetDevice(device) != hipSuccess) return PI_ERR_HIP;
+  pi_ffn f{*desc, &c, 0};
+  const XIn xin{x, nullptr, nullptr, 1, 0, nullptr};
+  return enqueue_layer(&c, &f, xin, x, B, y, mask, idx ? idx : c.idx, n_active ? n_active : c.nbuf, nullptr);
 }
 
 pi_status pi_compact(pi_ctx* ctx, const float* v, int32_t B, int32_t ffn, float threshold, uint64_t* mask,

@@ -166,6 +166,21 @@ pi_status pi_sparse_ffn(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B
 pi_status pi_layer(pi_ctx *ctx, const pi_ffn *ffn, const void *x, int32_t B, float *y,
                    uint64_t *mask, int32_t *idx, int32_t *n_active);
 
+/* pi_layer for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no pi_ctx, and no allocation at
+ * all. Its scratch (predictor stage 1 output, mask words, index list, activations, partial
+ * sums) is one fixed device array of the library, 26.1 MiB, which each GPU it runs on
+ * holds until the process ends. Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (several streams or threads) race; order them. No part of the array
+ * needs to start at zero. Limits: B <= 8 tokens, d <= 12288, ffn <= 49152, rank <= 1024
+ * (PI_ERR_UNSUPPORTED beyond them); otherwise the arguments, outputs, errors and kernels are
+ * those of pi_layer on a context of the same stream in union masking (the result is bitwise
+ * the same). PI_ERR_INVALID for a bad argument or description (no reason is kept: there is
+ * no context). Work is enqueued on hip_stream (NULL: the default stream) of `device`, which
+ * becomes the current device. */
+pi_status pi_layer_noalloc(int32_t device, void *hip_stream, const pi_ffn_desc *desc, const void *x,
+                           int32_t B, float *y, uint64_t *mask, int32_t *idx, int32_t *n_active);
+
 /* Threshold + compaction alone, on caller-provided decision values v [B][ffn] fp32:
  * the same device code pi_predict uses after computing v (P3 «Prediktor Kepadatan Adaptif»:
  * neurons predicted active are processed; P3 «Operator yang Sadar Neuron»: they are then

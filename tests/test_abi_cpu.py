@@ -62,6 +62,7 @@ def test_null_arguments_rejected_on_host():
     assert L.pi_predict(None, None, None, 1, None, None, None, None) == _lib.PI_ERR_INVALID
     assert L.pi_hot_first_order(None, 4, None) == _lib.PI_ERR_INVALID
     assert L.pi_ctx_set_mask_mode(None, 1) == _lib.PI_ERR_INVALID
+    assert L.pi_layer_noalloc(0, None, None, None, 1, None, None, None, None) == _lib.PI_ERR_INVALID
 
 
 @pytest.mark.parametrize("ffn", [5, 64, 4096])
