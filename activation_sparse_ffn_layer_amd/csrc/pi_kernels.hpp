@@ -68,6 +68,11 @@ struct XIn {
   int ny;
   int ystride;
   const float* c;
+  // ssq != nullptr (one token, predictor layers): y is already u = y - c, summed and centred
+  // by k_glue_sum, whose nsl slices' sums of squares ssq[s] = {sum y^2, sum u^2} give the
+  // divisor; stage 1 finishes the glue (k_stage1_g1)
+  const float* ssq;
+  int nsl;
 };
 
 // Element (t, c) of the glue's y, its partial sums added in order.
@@ -672,6 +677,135 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
       if (lane == 0 && t < B) z[(size_t)t * r + row] = s;
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// The glue between stacked layers at one token, in two steps, so that no workgroup of the
+// predictor reads the previous layer's G partial sums (G x d floats each).
+// k_glue_sum: workgroup s takes columns [4 * BLOCK * s, 4 * BLOCK * (s + 1)): y = the G
+// partial sums added in group order (as glue_x adds them), u = y - c, stored to u[col]
+// (fp32), and the slice's sums of squares ssq[s] = {sum of y^2, sum of u^2}.
+// k_stage1_g1: adds the slices' sums in slice order, x = fp16(u / sqrt(mean(u^2))) (x_prev
+// when y or u is all zero), stores x to x_out (workgroup 0) and computes z = W1 x: one wave
+// per row of W1, every chunk of the row issued at entry, behind the loads of u.
+// ---------------------------------------------------------------------------------------
+constexpr int GLUE_SLICES_MAX = 16;  // slices of k_glue_sum: d <= 4 * BLOCK * 16
+
+template <int G>
+__global__ __launch_bounds__(BLOCK) void k_glue_sum(const float* __restrict__ part, int gstride,
+                                                    const float* __restrict__ center, int d, float* __restrict__ u,
+                                                    float* __restrict__ ssq) {
+  __shared__ float red[2 * NWAVES];
+  const int n4 = d >> 2;
+  const int c = blockIdx.x * BLOCK + threadIdx.x;
+  const bool ok = c < n4;
+  const size_t off = 4 * (size_t)min(c, n4 - 1);
+  u32x4 p[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) p[g] = ld16_or0(part + (size_t)g * gstride + off, ok);
+  const u32x4 cv = (center != nullptr) ? ld16_or0(center + off, ok) : (u32x4){0, 0, 0, 0};
+  f32x4 y = __builtin_bit_cast(f32x4, p[0]);
+#pragma unroll
+  for (int g = 1; g < G; ++g) y += __builtin_bit_cast(f32x4, p[g]);
+  float ss = 0.f, su = 0.f;
+  u32x4 uo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float uv = y[e] - u2f(cv[e]);
+    ss = fmaf(y[e], y[e], ss);
+    su = fmaf(uv, uv, su);
+    uo[e] = __builtin_bit_cast(uint32_t, uv);
+  }
+  if (ok) *reinterpret_cast<u32x4*>(u + off) = uo;
+  block_sum2(ss, su, red);
+  if (threadIdx.x == 0) {
+    ssq[2 * blockIdx.x] = ss;
+    ssq[2 * blockIdx.x + 1] = su;
+  }
+}
+
+// PF: chunks of 16 bytes per lane in a W1 row (d <= 512 * PF); u is read as PF / 2 chunks
+// of 4 floats per thread.
+template <int PF>
+__global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __restrict__ u,
+                                                     const float* __restrict__ ssq, int nsl,
+                                                     const half_t* __restrict__ x_prev, half_t* __restrict__ x_out,
+                                                     float* __restrict__ z) {
+  constexpr int J = PF / 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  half_t* xs = reinterpret_cast<half_t*>(smem);
+  const int d = L.d, r = L.rank;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int row = blockIdx.x * NWAVES + wave;
+  const int n4 = d >> 2, nch = d >> 3;
+  // the slices' sums of squares (the same addresses in every thread), then u, then the row
+  u32x4 sq[GLUE_SLICES_MAX / 2];
+#pragma unroll
+  for (int k = 0; k < GLUE_SLICES_MAX / 2; ++k)
+    sq[k] = ld16_or0(ssq + 4 * min(k, (nsl - 1) / 2), 2 * k < nsl);
+  u32x4 uv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = threadIdx.x + BLOCK * j;
+    uv[j] = ld16_or0(u + 4 * (size_t)min(c, n4 - 1), c < n4);
+  }
+  const uint8_t* wrow = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
+  u32x4 wv[PF];
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    const int c = lane + WAVE * q;
+    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
+  }
+  float sy = 0.f, su = 0.f;
+#pragma unroll
+  for (int k = 0; k < GLUE_SLICES_MAX / 2; ++k) {
+    if (2 * k < nsl) {
+      sy += u2f(sq[k][0]);
+      su += u2f(sq[k][1]);
+    }
+    if (2 * k + 1 < nsl) {
+      sy += u2f(sq[k][2]);
+      su += u2f(sq[k][3]);
+    }
+  }
+  const float rr = glue_divisor(sy, su, d);
+  const bool out = blockIdx.x == 0;
+  // rr is the same in every thread: one branch, so the common case loads no x_prev
+  if (rr != 0.f) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = threadIdx.x + BLOCK * j;
+      if (c < n4) {
+        const half2_t h01 = {(half_t)(u2f(uv[j][0]) / rr), (half_t)(u2f(uv[j][1]) / rr)};
+        const half2_t h23 = {(half_t)(u2f(uv[j][2]) / rr), (half_t)(u2f(uv[j][3]) / rr)};
+        const uint2 o = {__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+        *reinterpret_cast<uint2*>(xs + 4 * c) = o;
+        if (out) *reinterpret_cast<uint2*>(x_out + 4 * c) = o;
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < nch; c += BLOCK) {
+      const u32x4 o = ld16(x_prev + 8 * c);
+      *reinterpret_cast<u32x4*>(xs + 8 * c) = o;
+      if (out) *reinterpret_cast<u32x4*>(x_out + 8 * c) = o;
+    }
+  }
+  __syncthreads();
+  if (row >= r) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    const int c = lane + WAVE * q;
+    if (c < nch) {
+      const u32x4 xv = ld16(xs + 8 * c);
+      acc = dot2(wv[q][0], xv[0], acc);
+      acc = dot2(wv[q][1], xv[1], acc);
+      acc = dot2(wv[q][2], xv[2], acc);
+      acc = dot2(wv[q][3], xv[3], acc);
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) z[row] = acc;
 }
 
 // ---------------------------------------------------------------------------------------

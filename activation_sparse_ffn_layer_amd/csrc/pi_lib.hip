@@ -38,6 +38,7 @@ struct pi_ctx {
   size_t hp_cap = 0;            // floats in hp
   float* part = nullptr;        // [32][max_batch][max_d] down-projection partial sums (groups or K splits)
   float* y = nullptr;           // [max_batch][max_d]
+  float* ssq = nullptr;         // [GLUE_SLICES_MAX][2]: k_glue_sum's slice sums of squares
   uint8_t* xbuf[2] = {nullptr, nullptr};  // [max_batch][max_d] fp32-sized
   uint8_t* xstage = nullptr;    // [max_batch][max_d] fp32-sized
   int32_t* nlog = nullptr;      // [NLOG_CAP]
@@ -185,7 +186,42 @@ pi_status launch_stage1_nb(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) 
   return PI_OK;
 }
 
+// Stage 1 at one token that finishes the glue started by k_glue_sum (xin.ssq != nullptr).
+template <int PF>
+pi_status launch_stage1_g1_t(pi_ctx* c, const LayerDev& L, const XIn& xin) {
+  const size_t lds = (size_t)L.d * 2;
+  PI_HIP(c, allow_lds(k_stage1_g1<PF>, lds));
+  const int grid = (L.rank + NWAVES - 1) / NWAVES;
+  PI_HIP(c, launch_k(c, K_STAGE1, k_stage1_g1<PF>, dim3(grid), lds, L, xin.y, xin.ssq, xin.nsl,
+                     static_cast<const half_t*>(xin.x), static_cast<half_t*>(xin.x_out), c->z));
+  return PI_OK;
+}
+
+// The two-step glue applies to one token of fp16 x with d <= 4 * BLOCK * GLUE_SLICES_MAX.
+bool glue_split_ok(int d, size_t xe) { return xe == 2 && d % 8 == 0 && d <= 4 * BLOCK * GLUE_SLICES_MAX; }
+
+// k_glue_sum over the previous layer's partial sums (one token): u into c->y, the slices'
+// sums of squares into c->ssq; returns the slice count through nsl.
+pi_status launch_glue_sum(pi_ctx* c, int d, const float* center, int* nsl) {
+  *nsl = (d / 4 + BLOCK - 1) / BLOCK;
+  const dim3 grid(*nsl);
+  switch (c->down_g) {
+    case 4: PI_HIP(c, launch_k(c, K_REDUCE, k_glue_sum<4>, grid, 0, c->part, d, center, d, c->y, c->ssq)); break;
+    case 8: PI_HIP(c, launch_k(c, K_REDUCE, k_glue_sum<8>, grid, 0, c->part, d, center, d, c->y, c->ssq)); break;
+    case 16: PI_HIP(c, launch_k(c, K_REDUCE, k_glue_sum<16>, grid, 0, c->part, d, center, d, c->y, c->ssq)); break;
+    default: return fail(c, PI_ERR_UNSUPPORTED, "glue over %d partial sums", c->down_g);
+  }
+  return PI_OK;
+}
+
 pi_status launch_stage1(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
+  if (xin.ssq != nullptr) {
+    if (B != 1 || !glue_split_ok(L.d, 2)) return fail(c, PI_ERR_INVALID, "split glue needs one token and d <= 16384");
+    if (L.d <= 512 * 8) return launch_stage1_g1_t<8>(c, L, xin);
+    if (L.d <= 512 * 16) return launch_stage1_g1_t<16>(c, L, xin);
+    if (L.d <= 512 * 24) return launch_stage1_g1_t<24>(c, L, xin);
+    return launch_stage1_g1_t<32>(c, L, xin);
+  }
   switch (nb_for(B)) {
     case 1: return launch_stage1_nb<1>(c, L, xin, B);
     case 2: return launch_stage1_nb<2>(c, L, xin, B);
@@ -503,7 +539,7 @@ pi_status launch_compact(pi_ctx* c, int ffn, int32_t* idx, int32_t* n) {
 // the stack runner's x buffers and count log. Batches above 8 tokens add the matrix-core
 // path's buffers.
 struct WsLayout {
-  size_t z, mt, mu, idx, n, a, hp, part, y, x0, x1, xs, nlog, zp, zh, zl, a16, total;
+  size_t z, mt, mu, idx, n, a, hp, part, y, ss, x0, x1, xs, nlog, zp, zh, zl, a16, total;
   size_t hp_floats, lda;
   bool mm;
 };
@@ -527,6 +563,7 @@ constexpr WsLayout ws_layout(int max_batch, int max_d, int max_ffn, int max_rank
   const size_t groups = o.mm ? (DOWN_G_WIDE > MM_KSD ? DOWN_G_WIDE : MM_KSD) : DOWN_G_WIDE;
   o.part = off; off += al256(groups * B * D * 4);
   o.y = off; off += al256(B * D * 4);
+  o.ss = off; off += al256((size_t)GLUE_SLICES_MAX * 2 * 4);
   o.x0 = off; off += stack ? al256(B * D * 4) : 0;
   o.x1 = off; off += stack ? al256(B * D * 4) : 0;
   o.xs = off; off += stack ? al256(B * D * 4) : 0;
@@ -554,6 +591,7 @@ void ws_assign(pi_ctx* c, uint8_t* ws, const WsLayout& o) {
   c->hp_cap = o.hp_floats;
   c->part = reinterpret_cast<float*>(ws + o.part);
   c->y = reinterpret_cast<float*>(ws + o.y);
+  c->ssq = reinterpret_cast<float*>(ws + o.ss);
   c->xbuf[0] = ws + o.x0;
   c->xbuf[1] = ws + o.x1;
   c->xstage = ws + o.xs;
@@ -1196,8 +1234,16 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
           x_cur = ctx->xbuf[l & 1];
         } else {
           const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-          // the glue adds the previous layer's partial sums itself
-          xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], ctx->down_g, B * d, center_into(l)};
+          if (layers[l]->desc.rank > 0 && glue_split_ok(d, xe)) {
+            // the partial sums are added once (k_glue_sum); the predictor's stage 1 finishes
+            // the glue from the centred sum and the slices' sums of squares
+            int nsl = 0;
+            PI_TRY(launch_glue_sum(ctx, d, center_into(l), &nsl));
+            xin = XIn{x_prev, ctx->y, ctx->xbuf[l & 1], 1, B * d, nullptr, ctx->ssq, nsl};
+          } else {
+            // the glue adds the previous layer's partial sums itself
+            xin = XIn{x_prev, ctx->part, ctx->xbuf[l & 1], ctx->down_g, B * d, center_into(l)};
+          }
           x_cur = ctx->xbuf[l & 1];
         }
         PI_TRY(enqueue_layer(ctx, layers[l], xin, x_cur, B, l == L - 1 ? ctx->y : nullptr, mask_out, idx_out,
