@@ -1271,6 +1271,159 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
   act_rounds_cols<WT, ACT, NB, XT>(L, cnt, id_of, xs, sw, cb, cb + cw, cw, stage, out);
 }
 
+// ---------------------------------------------------------------------------------------
+// k_up1 (one token): a_i = act(row_i . x + b_i) for the active neurons. One workgroup of
+// UP1_THREADS (16 waves) per CU: x is staged once per CU, and no workgroup's staging queues
+// behind another's row loads. The neurons are dealt out without a prefix scan. From the
+// union words, workgroup j takes the 16-bit units j, j + G, j + 2G, ... (unit u: bits
+// 16 (u % 4) .. 16 (u % 4) + 15 of word u / 4), so the dense words of a hot-first layout
+// spread over many workgroups; from an index list, it takes positions j, j + G, ... Each
+// wave takes RI items per round with every chunk of their rows in flight. Lane l takes chunks
+// l, l + 64, ... of each row (CPL of them; a chunk is 8 fp16 weights or one Q4_0 block) and
+// sums them as rows_dot does (its chunks ascending, then the wave sum), so a_i is bitwise
+// that of the other up kernels. ReGLU items are a gate and an up row.
+// ---------------------------------------------------------------------------------------
+constexpr int UP1_THREADS = 1024;
+constexpr int UP1_WAVES = UP1_THREADS / WAVE;
+constexpr int UP1_LIST = UP1_THREADS;  // list entries per workgroup: 64 units of 16 bits, or 1024 positions
+
+template <int WT, int ACT, int CPL, int RI>
+__global__ __launch_bounds__(UP1_THREADS) void k_up1(LayerDev L, const half_t* __restrict__ x,
+                                                     const uint64_t* __restrict__ words, int upw,
+                                                     const int32_t* __restrict__ idx_in,
+                                                     const int32_t* __restrict__ n_in, float* __restrict__ a) {
+  static_assert(WT == W_F16 || WT == W_Q4, "fp16 or Q4_0 rows");
+  constexpr int NRW = (ACT == ACT_REGLU) ? 2 : 1;  // rows per item
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  half_t* xs = reinterpret_cast<half_t*>(smem);                // [d]
+  int* il = reinterpret_cast<int*>(smem + (size_t)L.d * 2);     // [UP1_LIST]
+  __shared__ int wcnt[UP1_WAVES];
+  const int d = L.d, ffn = L.ffn, W = ffn >> 6;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int j = blockIdx.x, G = gridDim.x;
+  // this thread's candidate: bit (t % 16) of unit t / 16, or list position j + G t
+  int cand = -1;
+  if (words != nullptr) {
+    const int k = threadIdx.x >> 4, u = j + G * k;
+    const bool uok = k < upw && u < 4 * W;
+    const uint64_t word = uok ? words[u >> 2] : 0ull;
+    const int bit = 16 * (u & 3) + (threadIdx.x & 15);
+    if (uok && ((word >> bit) & 1ull)) cand = (u >> 2) * WAVE + bit;
+  } else {
+    const int n = min(max(*n_in, 0), ffn);
+    const int p = j + G * threadIdx.x;
+    const int i = (p < n) ? idx_in[p] : -1;
+    if ((unsigned)i < (unsigned)ffn) cand = i;
+  }
+  const int n16 = d >> 3;
+  for (int c = threadIdx.x; c < n16; c += UP1_THREADS)
+    *reinterpret_cast<u32x4*>(xs + 8 * c) = ld16(x + 8 * c);
+  // candidates in thread order: ballot within the wave, wave counts through LDS
+  const uint64_t bal = __ballot(cand >= 0);
+  if (lane == 0) wcnt[wave] = __popcll(bal);
+  __syncthreads();
+  int base = 0, cnt = 0;
+#pragma unroll
+  for (int w = 0; w < UP1_WAVES; ++w) {
+    base += (w < wave) ? wcnt[w] : 0;
+    cnt += wcnt[w];
+  }
+  if (cand >= 0) il[base + __popcll(bal & ((1ull << lane) - 1))] = cand;
+  __syncthreads();
+  constexpr int CH = (WT == W_Q4) ? 32 : 8;  // weights per chunk
+  const int nch = d / CH;
+  for (int k0 = wave; k0 < cnt; k0 += UP1_WAVES * RI) {
+    int ids[RI];
+#pragma unroll
+    for (int q = 0; q < RI; ++q) {
+      const int k = k0 + UP1_WAVES * q;
+      ids[q] = (k < cnt) ? il[k] : -1;
+    }
+    u32x4 w[RI][NRW][CPL];
+    float sc[RI][NRW][CPL];
+#pragma unroll
+    for (int q = 0; q < RI; ++q)
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        const uint8_t* base_w = (ACT == ACT_REGLU && r == 0) ? L.w_gate : L.w_up;
+        const uint16_t* base_s = (ACT == ACT_REGLU && r == 0) ? L.s_gate : L.s_up;
+        const size_t id = (size_t)(ids[q] >= 0 ? ids[q] : ids[0]);
+        const uint8_t* row = row_ptr<WT>(base_w, (int)id, d);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = lane + WAVE * c;
+          const int cc = min(ch, nch - 1);
+          const bool ok = ids[q] >= 0 && ch < nch;
+          w[q][r][c] = ld_stream_or0(row + (size_t)cc * 16, ok);
+          if constexpr (WT == W_Q4) {
+            const float sv = half_bits_to_float(base_s[id * (size_t)nch + cc]);
+            sc[q][r][c] = ok ? sv : 0.f;
+          }
+        }
+      }
+    float acc[RI][NRW];
+#pragma unroll
+    for (int q = 0; q < RI; ++q)
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) acc[q][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + WAVE * c;
+      if (ch < nch) {
+        if constexpr (WT == W_F16) {
+          const u32x4 xv = ld16(xs + ch * 8);
+#pragma unroll
+          for (int q = 0; q < RI; ++q)
+#pragma unroll
+            for (int r = 0; r < NRW; ++r) {
+              float sm = acc[q][r];
+              sm = dot2(w[q][r][c][0], xv[0], sm);
+              sm = dot2(w[q][r][c][1], xv[1], sm);
+              sm = dot2(w[q][r][c][2], xv[2], sm);
+              sm = dot2(w[q][r][c][3], xv[3], sm);
+              acc[q][r] = sm;
+            }
+        } else {
+          uint32_t xv[16];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x4 qv = ld16(xs + ch * 32 + 8 * m);
+            xv[4 * m + 0] = qv[0];
+            xv[4 * m + 1] = qv[1];
+            xv[4 * m + 2] = qv[2];
+            xv[4 * m + 3] = qv[3];
+          }
+#pragma unroll
+          for (int q = 0; q < RI; ++q)
+#pragma unroll
+            for (int r = 0; r < NRW; ++r) {
+              uint32_t wq[16];
+              q4_block_unpack(w[q][r][c], wq);
+              float sm = 0.f;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) sm = dot2(wq[e], xv[e], sm);
+              acc[q][r] = fmaf(sc[q][r][c], sm, acc[q][r]);
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RI; ++q) {
+      if (ids[q] < 0) break;
+      const float bias = L.b[ids[q]];
+      float v;
+      if constexpr (ACT != ACT_REGLU) {
+        v = act_one<ACT>(wave_sum(acc[q][0]) + bias);
+      } else {
+        const float g = wave_sum(acc[q][0]) + bias;
+        const float u = wave_sum(acc[q][1]);
+        v = fmaxf(g, 0.f) * u;
+      }
+      if (lane == 0) a[ids[q]] = v;
+    }
+  }
+}
+
 // a[t][i] = act(h + b_i) with h = the S slice partials of k_up_cols added in slice order
 // (ReGLU: max(h_gate + b_i, 0) * h_up), for the active neurons: the set bits of the union
 // words (thread k takes neuron k), or the index list (thread k takes entry k < n).
@@ -1327,9 +1480,9 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
 // Q4_0 (QS lanes per 32-element block): QS = 1: a lane takes a whole block (16 code bytes);
 // QS = 4: a lane takes 4 code bytes, i.e. elements 4j..4j+3 and 16+4j..16+4j+3 of the block.
 // ---------------------------------------------------------------------------------------
-template <int WT, int QS> struct DownGeom {
+template <int WT, int QS, int SQ = 4 * QS> struct DownGeom {
   static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32 / QS;  // columns per lane
-  static constexpr int SEG = (WT == W_Q4) ? 4 * QS : 8;                       // lanes per slice
+  static constexpr int SEG = (WT == W_Q4) ? SQ : 8;                           // lanes per slice
   static constexpr int SW = SEG * EPC;                                         // slice width (columns)
 };
 
@@ -1347,7 +1500,7 @@ __host__ __device__ constexpr int down_list_cap(int W, int G) { return (W + G - 
 // 176; OPT-175B at 8 tokens 52.1 -> 45.9 us per layer on MI355X), else the compiler's choice.
 template <int WT, int NB> struct DownWaves { static constexpr int value = (WT == W_Q4 && NB >= 8) ? 3 : 1; };
 
-template <int WT, int NB, bool SCAN, int U, int QS, int G>
+template <int WT, int NB, bool SCAN, int U, int QS, int G, int SQ = 4 * QS>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves<WT, NB>::value))) void k_down_part(LayerDev L, int B, const uint64_t* __restrict__ words,
                                                      const int32_t* __restrict__ idx_in,
                                                      const int32_t* __restrict__ n_in, const float* __restrict__ a,
@@ -1355,8 +1508,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
                                                      float* __restrict__ part, int32_t* __restrict__ idx_out,
                                                      int32_t* __restrict__ n_out, int32_t* __restrict__ n_log) {
   static_assert(G >= 1 && (G & (G - 1)) == 0, "the group count is a power of two");
-  constexpr int EPC = DownGeom<WT, QS>::EPC;
-  constexpr int SEG = DownGeom<WT, QS>::SEG;
+  constexpr int EPC = DownGeom<WT, QS, SQ>::EPC;
+  constexpr int SEG = DownGeom<WT, QS, SQ>::SEG;
   constexpr int SW = SEG * EPC;
   constexpr int NSL = BLOCK / SEG;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];

@@ -113,18 +113,22 @@ void prof_slot(pi_ctx* c, int klass, hipEvent_t* e0, hipEvent_t* e1) {
   *e1 = c->ev[2 * slot + 1];
 }
 
-// One kernel launch (BLOCK threads per workgroup) on the context's stream. When profiling,
+// One kernel launch (`block` threads per workgroup; BLOCK for launch_k) on the context's stream. When profiling,
 // the dispatch itself carries a pair of events (hipExtLaunchKernelGGL), so the pair times the
 // kernel's execution, not the queueing around it.
 template <typename... P, typename... A>
-hipError_t launch_k(pi_ctx* c, int klass, void (*kern)(P...), dim3 grid, size_t lds, A... args) {
+hipError_t launch_kb(pi_ctx* c, int klass, void (*kern)(P...), dim3 grid, int block, size_t lds, A... args) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (c->profiling) prof_slot(c, klass, &e0, &e1);
   if (e0 != nullptr)
-    hipExtLaunchKernelGGL(kern, grid, dim3(BLOCK), (uint32_t)lds, c->stream, e0, e1, 0u, static_cast<P>(args)...);
+    hipExtLaunchKernelGGL(kern, grid, dim3(block), (uint32_t)lds, c->stream, e0, e1, 0u, static_cast<P>(args)...);
   else
-    hipLaunchKernelGGL(kern, grid, dim3(BLOCK), lds, c->stream, static_cast<P>(args)...);
+    hipLaunchKernelGGL(kern, grid, dim3(block), lds, c->stream, static_cast<P>(args)...);
   return hipGetLastError();
+}
+template <typename... P, typename... A>
+hipError_t launch_k(pi_ctx* c, int klass, void (*kern)(P...), dim3 grid, size_t lds, A... args) {
+  return launch_kb(c, klass, kern, grid, BLOCK, lds, args...);
 }
 enum { K_STAGE1 = 0, K_STAGE2, K_TRUEMASK, K_UP, K_DOWN, K_REDUCE, K_COUNT };
 static_assert(K_COUNT == PI_KERNEL_CLASSES, "kernel classes out of sync with pi.h");
@@ -432,9 +436,63 @@ pi_status launch_up_cols_w(pi_ctx* c, const LayerDev& L, const void* x, int B, c
   }
 }
 
+// The one-token up kernel k_up1, for Q4_0 rows with d <= 2048 * 6 (blocks per lane rounded up
+// to an instantiated count; extra blocks are masked). Items per wave and round: about 64 VGPRs
+// of codes and scales in flight. The grid is one round of resident workgroups (one per CU),
+// at least one per 64 units of 16 bits. Measured on MI355X at the OPT-175B shape: 15.0 us per
+// layer against 18.3 us for k_up_cols; with 256-thread workgroups (3 per CU) 17.8 us, the
+// third workgroup on a CU staging x behind the others' row loads. fp16 rows stay on k_up_cols
+// (Falcon-40B 17.0 against 19.2 us, Llama-2-70B 27.4 against 29.0 us with 256-thread k_up1).
+template <int WT, int ACT, int CPL>
+constexpr int up1_ri() {
+  constexpr int per_item = (ACT == ACT_REGLU ? 2 : 1) * CPL * (WT == W_Q4 ? 5 : 4);
+  constexpr int ri = 64 / per_item;
+  return ri < 1 ? 1 : ri > 4 ? 4 : ri;
+}
+
+template <int ACT, int CPL>
+pi_status launch_up1_t(pi_ctx* c, const LayerDev& L, const void* x, const uint64_t* words, const int32_t* idx_in,
+                       const int32_t* n_in) {
+  const int W = L.ffn / 64;
+  const size_t lds = (size_t)L.d * 2 + UP1_LIST * 4;
+  auto kern = k_up1<W_Q4, ACT, CPL, up1_ri<W_Q4, ACT, CPL>()>;
+  PI_HIP(c, allow_lds(kern, lds));
+  int per_cu = 0;
+  PI_HIP(c, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, UP1_THREADS, lds));
+  const int resident = std::max(1, per_cu) * c->cus;
+  int grid, upw = 0;
+  if (words != nullptr) {
+    grid = std::min(4 * W, std::max((4 * W + UP1_THREADS / 16 - 1) / (UP1_THREADS / 16), resident));
+    upw = (4 * W + grid - 1) / grid;
+  } else {
+    grid = std::max((L.ffn + UP1_LIST - 1) / UP1_LIST, resident);
+  }
+  PI_HIP(c, launch_kb(c, K_UP, kern, dim3(grid), UP1_THREADS, lds, L, static_cast<const half_t*>(x), words, upw,
+                      idx_in, n_in, c->a));
+  return PI_OK;
+}
+
+template <int ACT>
+pi_status launch_up1_a(pi_ctx* c, const LayerDev& L, const void* x, const uint64_t* words, const int32_t* idx_in,
+                       const int32_t* n_in) {
+  const int cpl = (L.d + 2047) / 2048;
+  if (cpl <= 2) return launch_up1_t<ACT, 2>(c, L, x, words, idx_in, n_in);
+  if (cpl <= 4) return launch_up1_t<ACT, 4>(c, L, x, words, idx_in, n_in);
+  return launch_up1_t<ACT, 6>(c, L, x, words, idx_in, n_in);
+}
+
+bool up1_ok(const LayerDev& L, int B) { return B == 1 && L.wtype == W_Q4 && L.d <= 2048 * 6; }
+
 // a of the active neurons from the union words (words != nullptr) or an index list.
 pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
                          const int32_t* idx_in, const int32_t* n_in) {
+  if (up1_ok(L, B)) {
+    switch (L.act) {
+      case ACT_RELU: return launch_up1_a<ACT_RELU>(c, L, x, words, idx_in, n_in);
+      case ACT_REGLU: return launch_up1_a<ACT_REGLU>(c, L, x, words, idx_in, n_in);
+      default: return launch_up1_a<ACT_SQRELU>(c, L, x, words, idx_in, n_in);
+    }
+  }
   switch (L.act) {
     case ACT_RELU: return launch_up_cols_w<ACT_RELU>(c, L, x, B, words, idx_in, n_in);
     case ACT_REGLU: return launch_up_cols_w<ACT_REGLU>(c, L, x, B, words, idx_in, n_in);
@@ -453,23 +511,24 @@ constexpr int down_groups(int NB) { return NB >= 4 ? DOWN_G_WIDE : DOWN_G; }
 constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
 constexpr int MM_KSD = 32;  // K splits of the batched down projection
 
-template <int WT, int NB, bool SCAN, int G>
+template <int WT, int NB, bool SCAN, int G, int SQ = 0, int UO = 0>
 pi_status launch_down_g(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
                         int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
   constexpr int QS = (WT == W_Q4 && NB > 2) ? 4 : 1;
-  constexpr int U = (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
+  constexpr int SQE = SQ ? SQ : 4 * QS;
+  constexpr int U = UO ? UO : (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
   const int W = L.ffn / 64;
   // the group's list (+ its per-token bits), then the slots' column sums; or the compaction
   // block's words and prefix
-  constexpr size_t lds_red = (size_t)(BLOCK / DownGeom<WT, QS>::SEG) * (DownGeom<WT, QS>::SW + 1) * 4;
+  constexpr size_t lds_red = (size_t)(BLOCK / DownGeom<WT, QS, SQE>::SEG) * (DownGeom<WT, QS, SQE>::SW + 1) * 4;
   const size_t lds = std::max({(size_t)down_list_cap(W, G) * 5, lds_red,
                                SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : (size_t)0});
   constexpr size_t lds_static = 256;
   if (lds + lds_static > c->lds_max)
     return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the down projection", L.ffn);
-  auto kern = k_down_part<WT, NB, SCAN, U, QS, G>;
+  auto kern = k_down_part<WT, NB, SCAN, U, QS, G, SQE>;
   PI_HIP(c, allow_lds(kern, lds));
-  const int S = (L.d + DownGeom<WT, QS>::SW - 1) / DownGeom<WT, QS>::SW;
+  const int S = (L.d + DownGeom<WT, QS, SQE>::SW - 1) / DownGeom<WT, QS, SQE>::SW;
   // SCAN: one more block writes idx and n
   PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a, tok_mask,
                      c->part, idx_out, n_out, n_log));
@@ -488,6 +547,13 @@ pi_status launch_down_g(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
 template <int WT, int NB, bool SCAN>
 pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
                         int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
+  if constexpr (WT == W_Q4 && NB == 1) {
+    // Q4_0 rows at one token: 8 lanes (8 blocks, 128 code bytes) per neuron and slice, 16
+    // groups, 4 list items in flight per slot. Measured on MI355X at the OPT-175B shape against
+    // 4 lanes, 8 groups and 8 items: 19.8 -> 17.0 us per layer (8 items: 18.5; 16 lanes with
+    // 16 or 32 groups: 21-24; 4 lanes with 16 groups: 22).
+    return launch_down_g<WT, NB, SCAN, 16, 8, 4>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+  }
   if constexpr (WT != W_Q4 && NB <= 2) {
     if (L.d >= 8192)
       return launch_down_g<WT, NB, SCAN, DOWN_G_LONG>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
