@@ -687,7 +687,8 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
 // (fp32), and the slice's sums of squares ssq[s] = {sum of y^2, sum of u^2}.
 // k_stage1_g1: adds the slices' sums in slice order, x = fp16(u / sqrt(mean(u^2))) (x_prev
 // when y or u is all zero), stores x to x_out (workgroup 0) and computes z = W1 x: one wave
-// per row of W1, every chunk of the row issued at entry, behind the loads of u.
+// per row of W1, the row's first PRE chunks issued at entry (behind the loads of u), the rest
+// once x is formed.
 // ---------------------------------------------------------------------------------------
 constexpr int GLUE_SLICES_MAX = 16;  // slices of k_glue_sum: d <= 4 * BLOCK * 16
 
@@ -725,8 +726,8 @@ __global__ __launch_bounds__(BLOCK) void k_glue_sum(const float* __restrict__ pa
 }
 
 // PF: chunks of 16 bytes per lane in a W1 row (d <= 512 * PF); u is read as PF / 2 chunks
-// of 4 floats per thread.
-template <int PF>
+// of 4 floats per thread. PRE <= PF: chunks issued before x is formed.
+template <int PF, int PRE = PF>
 __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __restrict__ u,
                                                      const float* __restrict__ ssq, int nsl,
                                                      const half_t* __restrict__ x_prev, half_t* __restrict__ x_out,
@@ -752,7 +753,7 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
   const uint8_t* wrow = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
   u32x4 wv[PF];
 #pragma unroll
-  for (int q = 0; q < PF; ++q) {
+  for (int q = 0; q < PRE; ++q) {
     const int c = lane + WAVE * q;
     wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
   }
@@ -789,6 +790,12 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
       *reinterpret_cast<u32x4*>(xs + 8 * c) = o;
       if (out) *reinterpret_cast<u32x4*>(x_out + 8 * c) = o;
     }
+  }
+  // the rest of the row after x
+#pragma unroll
+  for (int q = PRE; q < PF; ++q) {
+    const int c = lane + WAVE * q;
+    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
   }
   __syncthreads();
   if (row >= r) return;
@@ -1272,75 +1279,83 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
 }
 
 // ---------------------------------------------------------------------------------------
-// k_up1 (one token): a_i = act(row_i . x + b_i) for the active neurons. One workgroup of
-// UP1_THREADS (16 waves) per CU: x is staged once per CU, and no workgroup's staging queues
-// behind another's row loads. The neurons are dealt out without a prefix scan. From the
-// union words, workgroup j takes the 16-bit units j, j + G, j + 2G, ... (unit u: bits
-// 16 (u % 4) .. 16 (u % 4) + 15 of word u / 4), so the dense words of a hot-first layout
-// spread over many workgroups; from an index list, it takes positions j, j + G, ... Each
-// wave takes RI items per round with every chunk of their rows in flight. Lane l takes chunks
-// l, l + 64, ... of each row (CPL of them; a chunk is 8 fp16 weights or one Q4_0 block) and
-// sums them as rows_dot does (its chunks ascending, then the wave sum), so a_i is bitwise
-// that of the other up kernels. ReGLU items are a gate and an up row.
+// k_upq: the gathered up (and gate) GEMV on Q4_0 rows for 1..8 tokens, one workgroup of
+// UPQ_THREADS (16 waves) per CU, over one column slice of x per workgroup. x is staged once
+// per workgroup, each 16-byte piece of a block's 32 columns stored so that the 64 lanes of a
+// wave, taking consecutive blocks, read consecutive 16-byte words (no LDS bank conflicts):
+// piece m of local block b of token t sits at ((t * 4 + m) * 64 * SB + b) * 8 halves. The
+// neurons are dealt out without a prefix scan: from the union words, the workgroups of chunk
+// c take the 16-bit units c, c + NC, c + 2 NC, ... (unit u: bits 16 (u % 4) .. 16 (u % 4) + 15
+// of word u / 4), so the dense words of a hot-first layout spread over many workgroups; from
+// an index list, positions c, c + NC, ... Lane l takes blocks l, l + 64, ... of the slice (SB
+// of them); a wave takes RI neurons per round with every block of their rows in flight. Each
+// (row, token) partial is the lane's blocks ascending, then the wave sum, as rows_dot. With
+// one slice (gridDim.x == 1) the kernel writes a itself, else the slice's partials go to
+// hp[s][r][t][i] for k_act_fin (r = 0: up row; ReGLU: 0 = gate, 1 = up).
 // ---------------------------------------------------------------------------------------
-constexpr int UP1_THREADS = 1024;
-constexpr int UP1_WAVES = UP1_THREADS / WAVE;
-constexpr int UP1_LIST = UP1_THREADS;  // list entries per workgroup: 64 units of 16 bits, or 1024 positions
+constexpr int UPQ_THREADS = 1024;
+constexpr int UPQ_WAVES = UPQ_THREADS / WAVE;
+constexpr int UPQ_LIST = UPQ_THREADS;  // list entries per workgroup: 64 units of 16 bits, or 1024 positions
 
-template <int WT, int ACT, int CPL, int RI>
-__global__ __launch_bounds__(UP1_THREADS) void k_up1(LayerDev L, const half_t* __restrict__ x,
+template <int ACT, int NB, int SB, int RI>
+__global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* __restrict__ x, int B,
                                                      const uint64_t* __restrict__ words, int upw,
                                                      const int32_t* __restrict__ idx_in,
-                                                     const int32_t* __restrict__ n_in, float* __restrict__ a) {
-  static_assert(WT == W_F16 || WT == W_Q4, "fp16 or Q4_0 rows");
-  constexpr int NRW = (ACT == ACT_REGLU) ? 2 : 1;  // rows per item
+                                                     const int32_t* __restrict__ n_in, float* __restrict__ hp,
+                                                     float* __restrict__ a) {
+  constexpr int NRW = (ACT == ACT_REGLU) ? 2 : 1;  // rows per neuron
+  constexpr int SLB = WAVE * SB;                    // blocks per slice
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  half_t* xs = reinterpret_cast<half_t*>(smem);                // [d]
-  int* il = reinterpret_cast<int*>(smem + (size_t)L.d * 2);     // [UP1_LIST]
-  __shared__ int wcnt[UP1_WAVES];
-  const int d = L.d, ffn = L.ffn, W = ffn >> 6;
+  half_t* xs = reinterpret_cast<half_t*>(smem);                                 // [NB][4][SLB][8]
+  int* il = reinterpret_cast<int*>(smem + (size_t)NB * 4 * SLB * 16);           // [UPQ_LIST]
+  __shared__ int wcnt[UPQ_WAVES];
+  const int d = L.d, ffn = L.ffn, W = ffn >> 6, nb = d >> 5;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int j = blockIdx.x, G = gridDim.x;
-  // this thread's candidate: bit (t % 16) of unit t / 16, or list position j + G t
+  const int s = blockIdx.x, S = gridDim.x, ch = blockIdx.y, NC = gridDim.y;
+  const int b0 = s * SLB;  // first block of the slice
+  // this thread's candidate neuron
   int cand = -1;
   if (words != nullptr) {
-    const int k = threadIdx.x >> 4, u = j + G * k;
+    const int k = threadIdx.x >> 4, u = ch + NC * k;
     const bool uok = k < upw && u < 4 * W;
     const uint64_t word = uok ? words[u >> 2] : 0ull;
     const int bit = 16 * (u & 3) + (threadIdx.x & 15);
     if (uok && ((word >> bit) & 1ull)) cand = (u >> 2) * WAVE + bit;
   } else {
     const int n = min(max(*n_in, 0), ffn);
-    const int p = j + G * threadIdx.x;
+    const int p = ch + NC * threadIdx.x;
     const int i = (p < n) ? idx_in[p] : -1;
     if ((unsigned)i < (unsigned)ffn) cand = i;
   }
-  const int n16 = d >> 3;
-  for (int c = threadIdx.x; c < n16; c += UP1_THREADS)
-    *reinterpret_cast<u32x4*>(xs + 8 * c) = ld16(x + 8 * c);
+  // x of the slice, swizzled (zeros past d and for tokens t >= B)
+  for (int e = threadIdx.x; e < NB * 4 * SLB; e += UPQ_THREADS) {
+    const int bl = e % SLB, m = (e / SLB) % 4, t = e / (4 * SLB);
+    const int blk = b0 + bl;
+    const bool ok = t < B && blk < nb;
+    const u32x4 v = ld16_or0(x + (size_t)min(t, B - 1) * d + (size_t)min(blk, nb - 1) * 32 + 8 * m, ok);
+    *reinterpret_cast<u32x4*>(xs + (size_t)((t * 4 + m) * SLB + bl) * 8) = v;
+  }
   // candidates in thread order: ballot within the wave, wave counts through LDS
   const uint64_t bal = __ballot(cand >= 0);
   if (lane == 0) wcnt[wave] = __popcll(bal);
   __syncthreads();
   int base = 0, cnt = 0;
 #pragma unroll
-  for (int w = 0; w < UP1_WAVES; ++w) {
+  for (int w = 0; w < UPQ_WAVES; ++w) {
     base += (w < wave) ? wcnt[w] : 0;
     cnt += wcnt[w];
   }
   if (cand >= 0) il[base + __popcll(bal & ((1ull << lane) - 1))] = cand;
   __syncthreads();
-  constexpr int CH = (WT == W_Q4) ? 32 : 8;  // weights per chunk
-  const int nch = d / CH;
-  for (int k0 = wave; k0 < cnt; k0 += UP1_WAVES * RI) {
+  for (int k0 = wave; k0 < cnt; k0 += UPQ_WAVES * RI) {
     int ids[RI];
 #pragma unroll
     for (int q = 0; q < RI; ++q) {
-      const int k = k0 + UP1_WAVES * q;
+      const int k = k0 + UPQ_WAVES * q;
       ids[q] = (k < cnt) ? il[k] : -1;
     }
-    u32x4 w[RI][NRW][CPL];
-    float sc[RI][NRW][CPL];
+    u32x4 w[RI][NRW][SB];
+    float sc[RI][NRW][SB];
 #pragma unroll
     for (int q = 0; q < RI; ++q)
 #pragma unroll
@@ -1348,46 +1363,39 @@ __global__ __launch_bounds__(UP1_THREADS) void k_up1(LayerDev L, const half_t* _
         const uint8_t* base_w = (ACT == ACT_REGLU && r == 0) ? L.w_gate : L.w_up;
         const uint16_t* base_s = (ACT == ACT_REGLU && r == 0) ? L.s_gate : L.s_up;
         const size_t id = (size_t)(ids[q] >= 0 ? ids[q] : ids[0]);
-        const uint8_t* row = row_ptr<WT>(base_w, (int)id, d);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int ch = lane + WAVE * c;
-          const int cc = min(ch, nch - 1);
-          const bool ok = ids[q] >= 0 && ch < nch;
-          w[q][r][c] = ld_stream_or0(row + (size_t)cc * 16, ok);
-          if constexpr (WT == W_Q4) {
-            const float sv = half_bits_to_float(base_s[id * (size_t)nch + cc]);
-            sc[q][r][c] = ok ? sv : 0.f;
-          }
+        for (int k = 0; k < SB; ++k) {
+          const int blk = b0 + lane + WAVE * k;
+          const int cb = min(blk, nb - 1);
+          const bool ok = ids[q] >= 0 && blk < nb && lane + WAVE * k < SLB;
+          w[q][r][k] = ld_stream_or0(base_w + (id * nb + cb) * 16, ok);
+          const float sv = half_bits_to_float(base_s[id * nb + cb]);
+          sc[q][r][k] = ok ? sv : 0.f;
         }
       }
-    float acc[RI][NRW];
+    float acc[RI][NRW][NB];
 #pragma unroll
     for (int q = 0; q < RI; ++q)
 #pragma unroll
-      for (int r = 0; r < NRW; ++r) acc[q][r] = 0.f;
+      for (int r = 0; r < NRW; ++r)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int ch = lane + WAVE * c;
-      if (ch < nch) {
-        if constexpr (WT == W_F16) {
-          const u32x4 xv = ld16(xs + ch * 8);
+        for (int t = 0; t < NB; ++t) acc[q][r][t] = 0.f;
 #pragma unroll
-          for (int q = 0; q < RI; ++q)
+    for (int k = 0; k < SB; ++k) {
+      const int bl = lane + WAVE * k;
+      if (b0 + bl < nb) {
+        // (q - 8) of every row's block as fp16 pairs, once for all tokens
+        uint32_t wq[RI][NRW][16];
 #pragma unroll
-            for (int r = 0; r < NRW; ++r) {
-              float sm = acc[q][r];
-              sm = dot2(w[q][r][c][0], xv[0], sm);
-              sm = dot2(w[q][r][c][1], xv[1], sm);
-              sm = dot2(w[q][r][c][2], xv[2], sm);
-              sm = dot2(w[q][r][c][3], xv[3], sm);
-              acc[q][r] = sm;
-            }
-        } else {
+        for (int q = 0; q < RI; ++q)
+#pragma unroll
+          for (int r = 0; r < NRW; ++r) q4_block_unpack(w[q][r][k], wq[q][r]);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
           uint32_t xv[16];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const u32x4 qv = ld16(xs + ch * 32 + 8 * m);
+            const u32x4 qv = ld16(xs + (size_t)((t * 4 + m) * SLB + bl) * 8);
             xv[4 * m + 0] = qv[0];
             xv[4 * m + 1] = qv[1];
             xv[4 * m + 2] = qv[2];
@@ -1397,12 +1405,10 @@ __global__ __launch_bounds__(UP1_THREADS) void k_up1(LayerDev L, const half_t* _
           for (int q = 0; q < RI; ++q)
 #pragma unroll
             for (int r = 0; r < NRW; ++r) {
-              uint32_t wq[16];
-              q4_block_unpack(w[q][r][c], wq);
               float sm = 0.f;
 #pragma unroll
-              for (int e = 0; e < 16; ++e) sm = dot2(wq[e], xv[e], sm);
-              acc[q][r] = fmaf(sc[q][r][c], sm, acc[q][r]);
+              for (int e = 0; e < 16; ++e) sm = dot2(wq[q][r][e], xv[e], sm);
+              acc[q][r][t] = fmaf(sc[q][r][k], sm, acc[q][r][t]);
             }
         }
       }
@@ -1410,16 +1416,30 @@ __global__ __launch_bounds__(UP1_THREADS) void k_up1(LayerDev L, const half_t* _
 #pragma unroll
     for (int q = 0; q < RI; ++q) {
       if (ids[q] < 0) break;
-      const float bias = L.b[ids[q]];
-      float v;
-      if constexpr (ACT != ACT_REGLU) {
-        v = act_one<ACT>(wave_sum(acc[q][0]) + bias);
+      const int i = ids[q];
+      if (S == 1) {
+        const float bias = L.b[i];
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          float v;
+          if constexpr (ACT != ACT_REGLU) {
+            v = act_one<ACT>(wave_sum(acc[q][0][t]) + bias);
+          } else {
+            const float g = wave_sum(acc[q][0][t]) + bias;
+            const float u = wave_sum(acc[q][1][t]);
+            v = fmaxf(g, 0.f) * u;
+          }
+          if (lane == t && t < B) a[(size_t)i * NB + t] = v;
+        }
       } else {
-        const float g = wave_sum(acc[q][0]) + bias;
-        const float u = wave_sum(acc[q][1]);
-        v = fmaxf(g, 0.f) * u;
+#pragma unroll
+        for (int r = 0; r < NRW; ++r)
+#pragma unroll
+          for (int t = 0; t < NB; ++t) {
+            const float v = wave_sum(acc[q][r][t]);
+            if (lane == t && t < B) hp[(((size_t)s * NRW + r) * B + t) * ffn + i] = v;
+          }
       }
-      if (lane == 0) a[ids[q]] = v;
     }
   }
 }

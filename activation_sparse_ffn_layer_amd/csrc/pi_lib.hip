@@ -191,12 +191,16 @@ pi_status launch_stage1_nb(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) 
 }
 
 // Stage 1 at one token that finishes the glue started by k_glue_sum (xin.ssq != nullptr).
+// The first 2/3 of the W1 row goes out at entry, behind u's loads; the rest once x is formed.
+// Measured on MI355X at the OPT-175B shape (d = 12288, 24 chunks per lane): 9.0 us with the
+// whole row issued at entry, 9.6 with none, 8.7 with 8 chunks, 8.2 with 16.
 template <int PF>
 pi_status launch_stage1_g1_t(pi_ctx* c, const LayerDev& L, const XIn& xin) {
   const size_t lds = (size_t)L.d * 2;
-  PI_HIP(c, allow_lds(k_stage1_g1<PF>, lds));
+  auto kern = k_stage1_g1<PF, PF * 2 / 3>;
+  PI_HIP(c, allow_lds(kern, lds));
   const int grid = (L.rank + NWAVES - 1) / NWAVES;
-  PI_HIP(c, launch_k(c, K_STAGE1, k_stage1_g1<PF>, dim3(grid), lds, L, xin.y, xin.ssq, xin.nsl,
+  PI_HIP(c, launch_k(c, K_STAGE1, kern, dim3(grid), lds, L, xin.y, xin.ssq, xin.nsl,
                      static_cast<const half_t*>(xin.x), static_cast<half_t*>(xin.x_out), c->z));
   return PI_OK;
 }
@@ -436,61 +440,88 @@ pi_status launch_up_cols_w(pi_ctx* c, const LayerDev& L, const void* x, int B, c
   }
 }
 
-// The one-token up kernel k_up1, for Q4_0 rows with d <= 2048 * 6 (blocks per lane rounded up
-// to an instantiated count; extra blocks are masked). Items per wave and round: about 64 VGPRs
-// of codes and scales in flight. The grid is one round of resident workgroups (one per CU),
-// at least one per 64 units of 16 bits. Measured on MI355X at the OPT-175B shape: 15.0 us per
-// layer against 18.3 us for k_up_cols; with 256-thread workgroups (3 per CU) 17.8 us, the
-// third workgroup on a CU staging x behind the others' row loads. fp16 rows stay on k_up_cols
-// (Falcon-40B 17.0 against 19.2 us, Llama-2-70B 27.4 against 29.0 us with 256-thread k_up1).
-template <int WT, int ACT, int CPL>
-constexpr int up1_ri() {
-  constexpr int per_item = (ACT == ACT_REGLU ? 2 : 1) * CPL * (WT == W_Q4 ? 5 : 4);
-  constexpr int ri = 64 / per_item;
-  return ri < 1 ? 1 : ri > 4 ? 4 : ri;
-}
+// The gathered up GEMV on Q4_0 rows at 1..8 tokens (k_upq): the slice of x (NB x 4 KB per
+// block per lane) stays within 128 KB of LDS, so one workgroup per CU; blocks per lane rounded
+// up to an instantiated count (extra blocks are masked); two neurons per wave and round. The
+// grid is one round of resident workgroups, at least one per 64 units of 16 bits. Measured on
+// MI355X at the OPT-175B shape and one token (before the swizzled x): 14.5 us per layer against
+// 18.3 us for k_up_cols; 33 us with 3 neurons per wave and round (registers spill); with
+// 256-thread workgroups (3 per CU) 17.8 us, the third workgroup on a CU staging x behind the
+// others' row loads. fp16 rows stay on k_up_cols (Falcon-40B 17.0 against 19.2 us,
+// Llama-2-70B 27.4 against 29.0 us with a 256-thread version of this kernel).
+constexpr size_t UPQ_X_BUDGET = 128 * 1024;
 
-template <int ACT, int CPL>
-pi_status launch_up1_t(pi_ctx* c, const LayerDev& L, const void* x, const uint64_t* words, const int32_t* idx_in,
-                       const int32_t* n_in) {
+template <int ACT, int NB, int SB>
+pi_status launch_upq_t(pi_ctx* c, const LayerDev& L, const void* x, int B, int S, const uint64_t* words,
+                       const int32_t* idx_in, const int32_t* n_in) {
+  constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
+  if (S > 1 && (size_t)S * NR * B * L.ffn > c->hp_cap)
+    return fail(c, PI_ERR_UNSUPPORTED, "layer %dx%d exceeds the context's slice buffer", L.d, L.ffn);
   const int W = L.ffn / 64;
-  const size_t lds = (size_t)L.d * 2 + UP1_LIST * 4;
-  auto kern = k_up1<W_Q4, ACT, CPL, up1_ri<W_Q4, ACT, CPL>()>;
+  const size_t lds = (size_t)NB * 4 * WAVE * SB * 16 + UPQ_LIST * 4;
+  auto kern = k_upq<ACT, NB, SB, 2>;
   PI_HIP(c, allow_lds(kern, lds));
   int per_cu = 0;
-  PI_HIP(c, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, UP1_THREADS, lds));
+  PI_HIP(c, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, UPQ_THREADS, lds));
   const int resident = std::max(1, per_cu) * c->cus;
-  int grid, upw = 0;
+  int nc, upw = 0;
   if (words != nullptr) {
-    grid = std::min(4 * W, std::max((4 * W + UP1_THREADS / 16 - 1) / (UP1_THREADS / 16), resident));
-    upw = (4 * W + grid - 1) / grid;
+    nc = std::min(4 * W, std::max((4 * W + UPQ_THREADS / 16 - 1) / (UPQ_THREADS / 16), std::max(1, resident / S)));
+    upw = (4 * W + nc - 1) / nc;
   } else {
-    grid = std::max((L.ffn + UP1_LIST - 1) / UP1_LIST, resident);
+    nc = std::max((L.ffn + UPQ_LIST - 1) / UPQ_LIST, std::max(1, resident / S));
   }
-  PI_HIP(c, launch_kb(c, K_UP, kern, dim3(grid), UP1_THREADS, lds, L, static_cast<const half_t*>(x), words, upw,
-                      idx_in, n_in, c->a));
+  PI_HIP(c, launch_kb(c, K_UP, kern, dim3(S, nc), UPQ_THREADS, lds, L, static_cast<const half_t*>(x), B, words, upw,
+                      idx_in, n_in, c->hp, c->a));
+  if (S > 1)
+    PI_HIP(c, launch_k(c, K_REDUCE, k_act_fin<ACT>, dim3((L.ffn + BLOCK - 1) / BLOCK), 0, L, B, S,
+                       (const float*)c->hp, words, idx_in, n_in, c->a));
   return PI_OK;
 }
 
-template <int ACT>
-pi_status launch_up1_a(pi_ctx* c, const LayerDev& L, const void* x, const uint64_t* words, const int32_t* idx_in,
-                       const int32_t* n_in) {
-  const int cpl = (L.d + 2047) / 2048;
-  if (cpl <= 2) return launch_up1_t<ACT, 2>(c, L, x, words, idx_in, n_in);
-  if (cpl <= 4) return launch_up1_t<ACT, 4>(c, L, x, words, idx_in, n_in);
-  return launch_up1_t<ACT, 6>(c, L, x, words, idx_in, n_in);
+// Slices and blocks per lane of k_upq for NB tokens; false where it does not apply.
+bool upq_geometry(const LayerDev& L, int NB, int* S, int* SB) {
+  if (L.wtype != W_Q4) return false;
+  const int nbl = (L.d / 32 + WAVE - 1) / WAVE;  // blocks per lane over the whole row
+  const int sb_max = (int)(UPQ_X_BUDGET / ((size_t)NB * 4 * WAVE * 16));
+  const int s = (nbl + sb_max - 1) / sb_max;
+  const int sb = (nbl + s - 1) / s;
+  if (sb > 6) return false;
+  *S = s;
+  *SB = sb <= 2 ? 2 : sb <= 3 ? 3 : 6;
+  return (size_t)NB * 4 * WAVE * *SB * 16 <= UPQ_X_BUDGET;
 }
 
-bool up1_ok(const LayerDev& L, int B) { return B == 1 && L.wtype == W_Q4 && L.d <= 2048 * 6; }
+template <int ACT, int NB>
+pi_status launch_upq_b(pi_ctx* c, const LayerDev& L, const void* x, int B, int S, int SB, const uint64_t* words,
+                       const int32_t* idx_in, const int32_t* n_in) {
+  switch (SB) {
+    case 2: return launch_upq_t<ACT, NB, 2>(c, L, x, B, S, words, idx_in, n_in);
+    case 3: return launch_upq_t<ACT, NB, 3>(c, L, x, B, S, words, idx_in, n_in);
+    default: return launch_upq_t<ACT, NB, 6>(c, L, x, B, S, words, idx_in, n_in);
+  }
+}
+
+template <int ACT>
+pi_status launch_upq_a(pi_ctx* c, const LayerDev& L, const void* x, int B, int S, int SB, const uint64_t* words,
+                       const int32_t* idx_in, const int32_t* n_in) {
+  switch (nb_for(B)) {
+    case 1: return launch_upq_b<ACT, 1>(c, L, x, B, S, SB, words, idx_in, n_in);
+    case 2: return launch_upq_b<ACT, 2>(c, L, x, B, S, SB, words, idx_in, n_in);
+    case 4: return launch_upq_b<ACT, 4>(c, L, x, B, S, SB, words, idx_in, n_in);
+    default: return launch_upq_b<ACT, 8>(c, L, x, B, S, SB, words, idx_in, n_in);
+  }
+}
 
 // a of the active neurons from the union words (words != nullptr) or an index list.
 pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
                          const int32_t* idx_in, const int32_t* n_in) {
-  if (up1_ok(L, B)) {
+  int S = 0, SB = 0;
+  if (B <= 8 && upq_geometry(L, nb_for(B), &S, &SB)) {
     switch (L.act) {
-      case ACT_RELU: return launch_up1_a<ACT_RELU>(c, L, x, words, idx_in, n_in);
-      case ACT_REGLU: return launch_up1_a<ACT_REGLU>(c, L, x, words, idx_in, n_in);
-      default: return launch_up1_a<ACT_SQRELU>(c, L, x, words, idx_in, n_in);
+      case ACT_RELU: return launch_upq_a<ACT_RELU>(c, L, x, B, S, SB, words, idx_in, n_in);
+      case ACT_REGLU: return launch_upq_a<ACT_REGLU>(c, L, x, B, S, SB, words, idx_in, n_in);
+      default: return launch_upq_a<ACT_SQRELU>(c, L, x, B, S, SB, words, idx_in, n_in);
     }
   }
   switch (L.act) {
@@ -557,6 +588,11 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   if constexpr (WT != W_Q4 && NB <= 2) {
     if (L.d >= 8192)
       return launch_down_g<WT, NB, SCAN, DOWN_G_LONG>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+  }
+  if constexpr (WT == W_Q4 && NB >= 4) {
+    // 8 groups at 4..8 tokens of Q4_0 rows: one round of resident workgroups at the OPT-175B
+    // shape (16 groups took two; 133 -> 128 us per layer at 8 tokens on MI355X)
+    return launch_down_g<WT, NB, SCAN, 8>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
   }
   return launch_down_g<WT, NB, SCAN, down_groups(NB)>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
 }
