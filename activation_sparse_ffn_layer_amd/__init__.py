@@ -16,7 +16,7 @@ import torch
 
 from ._lib import ACT, KERNEL_CLASSES, MASK_MODE, PI_OK, WTYPE, FfnDesc, PiError, StackDump, _ptr, lib
 
-__all__ = ["Context", "Ffn", "PiError", "predict", "sparse_ffn", "layer", "layer_noalloc", "compact", "glue", "stack_run",
+__all__ = ["Context", "Ffn", "PiError", "predict", "sparse_ffn", "layer", "layer_noalloc", "q4_dequant", "compact", "glue", "stack_run",
            "stack_run_dump", "stack_profile", "KERNEL_CLASSES",
            "hot_first_order", "permute_rows", "lib"]
 
@@ -124,6 +124,13 @@ def layer_noalloc(layer, x: torch.Tensor, y: torch.Tensor, mask: Optional[torch.
                                     _ptr(y), _ptr(mask), _ptr(idx), _ptr(n_active))
     if status != PI_OK:
         raise PiError(status, "pi_layer_noalloc failed")
+
+
+def q4_dequant(ctx: Context, codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor):
+    """pi_q4_dequant: Q4_0 rows (codes [rows][d/2] uint8, scales [rows][d/32] fp16 bits) to
+    out [rows][d] fp32 on the context's stream."""
+    rows, d = out.shape
+    ctx.check(lib().pi_q4_dequant(ctx.handle, _ptr(codes), _ptr(scales), rows, d, _ptr(out)))
 
 
 def compact(ctx: Context, v: torch.Tensor, threshold: float, mask: torch.Tensor, idx: torch.Tensor,

@@ -50,6 +50,7 @@ _SIGS = {
     "pi_layer": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "pi_layer_noalloc": (c_int32, [c_int32, c_void_p, POINTER(FfnDesc), c_void_p, c_int32, c_void_p, c_void_p,
                                    c_void_p, c_void_p]),
+    "pi_q4_dequant": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
     "pi_compact": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p]),
     "pi_glue": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p]),
     "pi_stack_run": (c_int32, [c_void_p, POINTER(c_void_p), c_int32, c_void_p, c_int32, c_int32, c_void_p,

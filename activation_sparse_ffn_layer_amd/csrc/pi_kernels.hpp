@@ -1279,8 +1279,8 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
 }
 
 // ---------------------------------------------------------------------------------------
-// k_upq: the gathered up (and gate) GEMV on Q4_0 rows for 1..8 tokens, one workgroup of
-// UPQ_THREADS (16 waves) per CU, over one column slice of x per workgroup. x is staged once
+// k_upq: the gathered up (and gate) GEMV on Q4_0 rows for 1..8 tokens, one workgroup of NTH
+// threads per CU, over one column slice of x per workgroup. x is staged once
 // per workgroup, each 16-byte piece of a block's 32 columns stored so that the 64 lanes of a
 // wave, taking consecutive blocks, read consecutive 16-byte words (no LDS bank conflicts):
 // piece m of local block b of token t sits at ((t * 4 + m) * 64 * SB + b) * 8 halves. The
@@ -1293,22 +1293,28 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
 // one slice (gridDim.x == 1) the kernel writes a itself, else the slice's partials go to
 // hp[s][r][t][i] for k_act_fin (r = 0: up row; ReGLU: 0 = gate, 1 = up).
 // ---------------------------------------------------------------------------------------
-constexpr int UPQ_THREADS = 1024;
-constexpr int UPQ_WAVES = UPQ_THREADS / WAVE;
-constexpr int UPQ_LIST = UPQ_THREADS;  // list entries per workgroup: 64 units of 16 bits, or 1024 positions
+constexpr int UPQ_LIST = 1024;  // list entries per workgroup: NTH / 16 units of 16 bits, or NTH positions
 
-template <int ACT, int NB, int SB, int RI>
-__global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* __restrict__ x, int B,
-                                                     const uint64_t* __restrict__ words, int upw,
-                                                     const int32_t* __restrict__ idx_in,
-                                                     const int32_t* __restrict__ n_in, float* __restrict__ hp,
-                                                     float* __restrict__ a) {
+// A buffer resource over `bytes` bytes at base (raw 32-bit data format): a load at an offset
+// past `bytes` returns zeros and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t BUF_OOB = 0x80000000u;  // an offset past every resource here
+
+template <int ACT, int NB, int SB, int RI, int NTH>
+__global__ __launch_bounds__(NTH) void k_upq(LayerDev L, const half_t* __restrict__ x, int B,
+                                             const uint64_t* __restrict__ words, int upw,
+                                             const int32_t* __restrict__ idx_in, const int32_t* __restrict__ n_in,
+                                             float* __restrict__ hp, float* __restrict__ a) {
   constexpr int NRW = (ACT == ACT_REGLU) ? 2 : 1;  // rows per neuron
   constexpr int SLB = WAVE * SB;                    // blocks per slice
+  constexpr int NW = NTH / WAVE;
+  static_assert(NTH <= UPQ_LIST, "one candidate per thread");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);                                 // [NB][4][SLB][8]
-  int* il = reinterpret_cast<int*>(smem + (size_t)NB * 4 * SLB * 16);           // [UPQ_LIST]
-  __shared__ int wcnt[UPQ_WAVES];
+  int* il = reinterpret_cast<int*>(smem + (size_t)NB * 4 * SLB * 16);           // [NTH]
+  __shared__ int wcnt[NW];
   const int d = L.d, ffn = L.ffn, W = ffn >> 6, nb = d >> 5;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int s = blockIdx.x, S = gridDim.x, ch = blockIdx.y, NC = gridDim.y;
@@ -1328,7 +1334,7 @@ __global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* _
     if ((unsigned)i < (unsigned)ffn) cand = i;
   }
   // x of the slice, swizzled (zeros past d and for tokens t >= B)
-  for (int e = threadIdx.x; e < NB * 4 * SLB; e += UPQ_THREADS) {
+  for (int e = threadIdx.x; e < NB * 4 * SLB; e += NTH) {
     const int bl = e % SLB, m = (e / SLB) % 4, t = e / (4 * SLB);
     const int blk = b0 + bl;
     const bool ok = t < B && blk < nb;
@@ -1341,38 +1347,40 @@ __global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* _
   __syncthreads();
   int base = 0, cnt = 0;
 #pragma unroll
-  for (int w = 0; w < UPQ_WAVES; ++w) {
+  for (int w = 0; w < NW; ++w) {
     base += (w < wave) ? wcnt[w] : 0;
     cnt += wcnt[w];
   }
   if (cand >= 0) il[base + __popcll(bal & ((1ull << lane) - 1))] = cand;
   __syncthreads();
-  for (int k0 = wave; k0 < cnt; k0 += UPQ_WAVES * RI) {
-    int ids[RI];
+  // the rows: codes and scales through bounds-checked buffer loads (a missing item or block
+  // past d loads zeros without touching memory)
+  __amdgpu_buffer_rsrc_t rw[NRW], rs[NRW];
+#pragma unroll
+  for (int r = 0; r < NRW; ++r) {
+    const bool gate = ACT == ACT_REGLU && r == 0;
+    rw[r] = buf_rsrc(gate ? L.w_gate : L.w_up, (uint32_t)((size_t)ffn * nb * 16));
+    rs[r] = buf_rsrc(gate ? L.s_gate : L.s_up, (uint32_t)((size_t)ffn * nb * 2));
+  }
+  constexpr int STEP = NW * RI;
+  auto load = [&](int k0, int (&ids)[RI], u32x4 (&w)[RI][NRW][SB], uint32_t (&sc)[RI][NRW][SB]) {
 #pragma unroll
     for (int q = 0; q < RI; ++q) {
-      const int k = k0 + UPQ_WAVES * q;
+      const int k = k0 + NW * q;
       ids[q] = (k < cnt) ? il[k] : -1;
-    }
-    u32x4 w[RI][NRW][SB];
-    float sc[RI][NRW][SB];
 #pragma unroll
-    for (int q = 0; q < RI; ++q)
+      for (int r = 0; r < NRW; ++r)
 #pragma unroll
-      for (int r = 0; r < NRW; ++r) {
-        const uint8_t* base_w = (ACT == ACT_REGLU && r == 0) ? L.w_gate : L.w_up;
-        const uint16_t* base_s = (ACT == ACT_REGLU && r == 0) ? L.s_gate : L.s_up;
-        const size_t id = (size_t)(ids[q] >= 0 ? ids[q] : ids[0]);
-#pragma unroll
-        for (int k = 0; k < SB; ++k) {
-          const int blk = b0 + lane + WAVE * k;
-          const int cb = min(blk, nb - 1);
-          const bool ok = ids[q] >= 0 && blk < nb && lane + WAVE * k < SLB;
-          w[q][r][k] = ld_stream_or0(base_w + (id * nb + cb) * 16, ok);
-          const float sv = half_bits_to_float(base_s[id * nb + cb]);
-          sc[q][r][k] = ok ? sv : 0.f;
+        for (int kb = 0; kb < SB; ++kb) {
+          const int blk = b0 + lane + WAVE * kb;
+          const bool ok = ids[q] >= 0 && blk < nb && lane + WAVE * kb < SLB;
+          const uint32_t e = (uint32_t)ids[q] * (uint32_t)nb + (uint32_t)blk;
+          w[q][r][kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[r], ok ? e * 16u : BUF_OOB, 0, 2));
+          sc[q][r][kb] = __builtin_amdgcn_raw_buffer_load_b16(rs[r], ok ? e * 2u : BUF_OOB, 0, 0);
         }
-      }
+    }
+  };
+  auto compute = [&](const int (&ids)[RI], const u32x4 (&w)[RI][NRW][SB], const uint32_t (&sc)[RI][NRW][SB]) {
     float acc[RI][NRW][NB];
 #pragma unroll
     for (int q = 0; q < RI; ++q)
@@ -1381,15 +1389,19 @@ __global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* _
 #pragma unroll
         for (int t = 0; t < NB; ++t) acc[q][r][t] = 0.f;
 #pragma unroll
-    for (int k = 0; k < SB; ++k) {
-      const int bl = lane + WAVE * k;
+    for (int kb = 0; kb < SB; ++kb) {
+      const int bl = lane + WAVE * kb;
       if (b0 + bl < nb) {
         // (q - 8) of every row's block as fp16 pairs, once for all tokens
         uint32_t wq[RI][NRW][16];
+        float scf[RI][NRW];
 #pragma unroll
         for (int q = 0; q < RI; ++q)
 #pragma unroll
-          for (int r = 0; r < NRW; ++r) q4_block_unpack(w[q][r][k], wq[q][r]);
+          for (int r = 0; r < NRW; ++r) {
+            q4_block_unpack(w[q][r][kb], wq[q][r]);
+            scf[q][r] = half_bits_to_float((uint16_t)sc[q][r][kb]);
+          }
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           uint32_t xv[16];
@@ -1408,7 +1420,7 @@ __global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* _
               float sm = 0.f;
 #pragma unroll
               for (int e = 0; e < 16; ++e) sm = dot2(wq[q][r][e], xv[e], sm);
-              acc[q][r][t] = fmaf(sc[q][r][k], sm, acc[q][r][t]);
+              acc[q][r][t] = fmaf(scf[q][r], sm, acc[q][r][t]);
             }
         }
       }
@@ -1441,6 +1453,13 @@ __global__ __launch_bounds__(UPQ_THREADS) void k_upq(LayerDev L, const half_t* _
           }
       }
     }
+  };
+  for (int k0 = wave; k0 < cnt; k0 += STEP) {
+    int ids[RI];
+    u32x4 w[RI][NRW][SB];
+    uint32_t sc[RI][NRW][SB];
+    load(k0, ids, w, sc);
+    compute(ids, w, sc);
   }
 }
 
@@ -1490,8 +1509,9 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
 // scheduling. (Adding them here, in the last workgroup of each slice, needs a device-scope
 // release per workgroup: an L2 write-back that costs far more than the separate pass.)
 //  SCAN: the group's neurons come from the union words (no workgroup needs the others'
-//        counts). One extra workgroup (the last block) prefix-scans all the words and writes
-//        the ascending index list idx and n.
+//        counts). One extra workgroup (block 0, dispatched first, so it never waits for a
+//        slot behind a full round of the others) prefix-scans all the words and writes the
+//        ascending index list idx and n.
 //  else: the given index list, filtered to the group's words in list order (an ascending
 //        list gives the same group lists, hence the same y, as SCAN).
 // tok_mask != nullptr (per-token masking, SCAN only): a[t][i] counts only where bit i of
@@ -1500,6 +1520,17 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
 // Q4_0 (QS lanes per 32-element block): QS = 1: a lane takes a whole block (16 code bytes);
 // QS = 4: a lane takes 4 code bytes, i.e. elements 4j..4j+3 and 16+4j..16+4j+3 of the block.
 // ---------------------------------------------------------------------------------------
+// v of lane j of this lane's quad (DPP quad permutation; the quad's lanes must be active).
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int j) {
+  const int x = (int)v;
+  switch (j) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, false);
+  }
+}
+
 template <int WT, int QS, int SQ = 4 * QS> struct DownGeom {
   static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32 / QS;  // columns per lane
   static constexpr int SEG = (WT == W_Q4) ? SQ : 8;                           // lanes per slice
@@ -1540,7 +1571,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
   // per-token masking: bit t of tb[j] = token t's mask bit of neuron il[j]
   uint8_t* tb = reinterpret_cast<uint8_t*>(il + down_list_cap(W, G));
   if constexpr (SCAN) {
-    if (blockIdx.x == gridDim.x - 1) {  // the compaction block: ascending idx and n
+    if (blockIdx.x == 0) {  // the compaction block (dispatched first): ascending idx and n
       uint64_t* wl = reinterpret_cast<uint64_t*>(smem);
       int* pre = reinterpret_cast<int*>(wl + W);
       const int n = scan_words(words, W, wl, pre, red);
@@ -1559,7 +1590,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
       return;
     }
   }
-  const int g = blockIdx.x % G, s = blockIdx.x / G;
+  const int bid = SCAN ? (int)blockIdx.x - 1 : (int)blockIdx.x;  // SCAN: block 0 compacts
+  const int g = bid % G, s = bid / G;
   const int slot = threadIdx.x / SEG, sl = threadIdx.x % SEG;
   // the first column this lane touches; Q4 lanes of one block share a block index
   const int col0 = s * SW + ((WT == W_Q4 && QS == 4) ? (sl >> 2) * 32 : sl * EPC);
@@ -1631,28 +1663,43 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
       ii[u] = (j < ng) ? il[j] : -1;
       tbits[u] = (SCAN && tok_mask != nullptr && j < ng) ? tb[j] : 0xFFu;
     }
-    // activations first (small, likely cached; a neuron's NB tokens are contiguous), then the rows
-    float av[U][NB];
+    // activations first (small, likely cached; a neuron's NB tokens are contiguous), then the
+    // rows. With quarter blocks (QPAIR), each lane of a block's quad takes TPL = NB / 4 tokens
+    // and forms their a * s, which the quad's lanes then share.
+    constexpr bool QPAIR = WT == W_Q4 && QS == 4;
+    constexpr int TPL = QPAIR ? NB / 4 : NB;
+    const int qd = sl & 3;  // lane within the block's quad (QPAIR)
+    float av[U][TPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float* ap = a + (size_t)(ii[u] >= 0 ? ii[u] : 0) * NB;
-      if constexpr (NB >= 4) {
+      if constexpr (QPAIR) {
 #pragma unroll
-        for (int t4 = 0; t4 < NB; t4 += 4) {
-          const u32x4 v4 = ld16(ap + t4);  // zeroed below where ii[u] < 0
-#pragma unroll
-          for (int e = 0; e < 4; ++e) av[u][t4 + e] = u2f(v4[e]);
+        for (int h = 0; h < TPL; ++h) {
+          const int t = TPL * qd + h;
+          const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
+          const float v = ap[t];
+          av[u][h] = on ? v : 0.f;
         }
       } else {
+        if constexpr (NB >= 4) {
 #pragma unroll
-        for (int t = 0; t < NB; ++t) av[u][t] = ap[t];  // zeroed below where ii[u] < 0
-      }
+          for (int t4 = 0; t4 < NB; t4 += 4) {
+            const u32x4 v4 = ld16(ap + t4);  // zeroed below where ii[u] < 0
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        // tokens past B hold no value; per-token masking: token t takes neuron i only if its
-        // own mask has it
-        const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
-        av[u][t] = on ? av[u][t] : 0.f;
+            for (int e = 0; e < 4; ++e) av[u][t4 + e] = u2f(v4[e]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NB; ++t) av[u][t] = ap[t];  // zeroed below where ii[u] < 0
+        }
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          // tokens past B hold no value; per-token masking: token t takes neuron i only if its
+          // own mask has it
+          const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
+          av[u][t] = on ? av[u][t] : 0.f;
+        }
       }
     }
     u32x4 w[U];
@@ -1728,10 +1775,16 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
         pr[5] = q4_pair(h01, SEL_B23);
         pr[6] = q4_pair(h23, SEL_B01);
         pr[7] = q4_pair(h23, SEL_B23);
+        // this lane's tokens' fp16 pairs of a * s, then every token's from its quad lane
+        uint32_t pp[TPL];
+#pragma unroll
+        for (int h = 0; h < TPL; ++h) {
+          const half_t su = (half_t)(av[u][h] * sc[u]), sv = (half_t)(av[u + 1][h] * sc[u + 1]);
+          pp[h] = __builtin_bit_cast(uint32_t, (half2_t){su, sv});
+        }
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
-          const half_t su = (half_t)(av[u][t] * sc[u]), sv = (half_t)(av[u + 1][t] * sc[u + 1]);
-          const uint32_t ap = __builtin_bit_cast(uint32_t, (half2_t){su, sv});
+          const uint32_t ap = quad_bcast(pp[t % TPL], t / TPL);
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[t][e] = dot2(pr[e], ap, acc[t][e]);
         }
@@ -1838,6 +1891,25 @@ __global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, con
 #pragma unroll
         for (int e = 0; e < 4; ++e) xo[4 * c + e] = (XT)((u2f(v[j][e]) - u2f(cv[j][e])) / r);
     }
+  }
+}
+
+// out[e] = (q - 8) * s for the 32 elements of block e (one block per thread): the (q - 8)
+// fp16 pairs of q4_block_unpack, times the block's scale in fp32 (exact).
+__global__ __launch_bounds__(BLOCK) void k_q4_dequant(const uint8_t* __restrict__ codes,
+                                                      const uint16_t* __restrict__ scales, long long nblocks,
+                                                      float* __restrict__ out) {
+  const long long e = (long long)blockIdx.x * BLOCK + threadIdx.x;
+  if (e >= nblocks) return;
+  uint32_t wq[16];
+  q4_block_unpack(ld16(codes + e * 16), wq);
+  const float s = half_bits_to_float(scales[e]);
+  float* o = out + e * 32;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const half2_t h = __builtin_bit_cast(half2_t, wq[m]);
+    o[2 * m] = (float)h[0] * s;
+    o[2 * m + 1] = (float)h[1] * s;
   }
 }
 

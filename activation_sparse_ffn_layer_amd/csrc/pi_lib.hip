@@ -458,20 +458,26 @@ pi_status launch_upq_t(pi_ctx* c, const LayerDev& L, const void* x, int B, int S
   if (S > 1 && (size_t)S * NR * B * L.ffn > c->hp_cap)
     return fail(c, PI_ERR_UNSUPPORTED, "layer %dx%d exceeds the context's slice buffer", L.d, L.ffn);
   const int W = L.ffn / 64;
-  const size_t lds = (size_t)NB * 4 * WAVE * SB * 16 + UPQ_LIST * 4;
-  auto kern = k_upq<ACT, NB, SB, 2>;
+  // 16 waves, two neurons per wave and round. Measured on MI355X at the OPT-175B shape and 8
+  // tokens: 86.6 us per layer; 12 waves with the next round's rows loading during this one's
+  // arithmetic 88.5 us; 8 waves with 4 neurons per round (half the LDS reads of x), pipelined,
+  // 102 us. The kernel is VALU- and LDS-bound there: about 180 VALU instructions per block and
+  // row (16 dot2 per token), 57% VALU-busy.
+  constexpr int NTH = 1024;
+  const size_t lds = (size_t)NB * 4 * WAVE * SB * 16 + (size_t)NTH * 4;
+  auto kern = k_upq<ACT, NB, SB, 2, NTH>;
   PI_HIP(c, allow_lds(kern, lds));
   int per_cu = 0;
-  PI_HIP(c, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, UPQ_THREADS, lds));
+  PI_HIP(c, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NTH, lds));
   const int resident = std::max(1, per_cu) * c->cus;
   int nc, upw = 0;
   if (words != nullptr) {
-    nc = std::min(4 * W, std::max((4 * W + UPQ_THREADS / 16 - 1) / (UPQ_THREADS / 16), std::max(1, resident / S)));
+    nc = std::min(4 * W, std::max((4 * W + NTH / 16 - 1) / (NTH / 16), std::max(1, resident / S)));
     upw = (4 * W + nc - 1) / nc;
   } else {
-    nc = std::max((L.ffn + UPQ_LIST - 1) / UPQ_LIST, std::max(1, resident / S));
+    nc = std::max((L.ffn + NTH - 1) / NTH, std::max(1, resident / S));
   }
-  PI_HIP(c, launch_kb(c, K_UP, kern, dim3(S, nc), UPQ_THREADS, lds, L, static_cast<const half_t*>(x), B, words, upw,
+  PI_HIP(c, launch_kb(c, K_UP, kern, dim3(S, nc), NTH, lds, L, static_cast<const half_t*>(x), B, words, upw,
                       idx_in, n_in, c->hp, c->a));
   if (S > 1)
     PI_HIP(c, launch_k(c, K_REDUCE, k_act_fin<ACT>, dim3((L.ffn + BLOCK - 1) / BLOCK), 0, L, B, S,
@@ -1185,6 +1191,21 @@ pi_status pi_layer_noalloc(int32_t device, void* hip_stream, const pi_ffn_desc* 
   pi_ffn f{*desc, &c, 0};
   const XIn xin{x, nullptr, nullptr, 1, 0, nullptr};
   return enqueue_layer(&c, &f, xin, x, B, y, mask, idx ? idx : c.idx, n_active ? n_active : c.nbuf, nullptr);
+}
+
+pi_status pi_q4_dequant(pi_ctx* ctx, const uint8_t* codes, const uint16_t* scales, int32_t rows, int32_t d,
+                        float* out) {
+  if (ctx == nullptr) return PI_ERR_INVALID;
+  if (rows < 0 || d <= 0 || d % 32) return fail(ctx, PI_ERR_INVALID, "rows %d, d %d: need rows >= 0 and d %% 32 == 0", rows, d);
+  PI_TRY(check_dev_ptr(ctx, codes, "codes"));
+  PI_TRY(check_dev_ptr(ctx, scales, "scales"));
+  PI_TRY(check_dev_ptr(ctx, out, "out"));
+  if (rows == 0) return PI_OK;
+  PI_HIP(ctx, hipSetDevice(ctx->device));
+  const long long nblocks = (long long)rows * (d / 32);
+  PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_q4_dequant, dim3((unsigned)((nblocks + BLOCK - 1) / BLOCK)), 0, codes, scales,
+                       nblocks, out));
+  return PI_OK;
 }
 
 pi_status pi_compact(pi_ctx* ctx, const float* v, int32_t B, int32_t ffn, float threshold, uint64_t* mask,

@@ -257,6 +257,18 @@ pi_status pi_stack_profile(pi_ctx *ctx, const pi_ffn *const *layers, int32_t L, 
                            int32_t T, int32_t B, float *y_out, int32_t *n_active_log, double *ms_out,
                            int64_t *launches_out);
 
+/* Q4_0 rows to fp32 with the kernels' own in-register unpacking (P1 «Kuantizasyon ve
+ * uyumluluk»: 4-bit weights in 32-element blocks with a 16-bit scale): out[i][c] =
+ * (q - 8) * s for every row i < rows and column c < d, where block b of row i is the 16
+ * code bytes codes[(i * d/32 + b) * 16 ...] (byte j: element j in the low nibble, element
+ * j + 16 in the high nibble) and its scale is the fp16 scales[i * d/32 + b]. (q - 8) is
+ * rebuilt exactly in fp16 and multiplied by the scale in fp32, which is exact (a 4-bit by an
+ * 11-bit significand), so the result is bitwise the dequantised weight. Device pointers:
+ * codes [rows][d/2] bytes, scales [rows][d/32] fp16, out [rows][d] fp32. d % 32 == 0. For
+ * checking the dequantisation against a plain implementation. */
+pi_status pi_q4_dequant(pi_ctx *ctx, const uint8_t *codes, const uint16_t *scales, int32_t rows, int32_t d,
+                        float *out);
+
 /* Hot-first neuron order (P3 «Penempatan dan Pengelolaan Neuron»): perm[k] = the neuron
  * with the k-th largest activation probability, ties in ascending neuron order. HOST
  * pointers: p double [ffn], perm int32 [ffn]. */

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 COMPUTE_CALLS = ("pi_predict", "pi_sparse_ffn", "pi_layer", "pi_compact", "pi_glue", "pi_stack_run",
-                 "pi_stack_run_dump", "pi_stack_profile", "pi_hot_first_order", "pi_permute_rows")
+                 "pi_stack_run_dump", "pi_stack_profile", "pi_hot_first_order", "pi_permute_rows", "pi_q4_dequant")
 
 
 def test_every_compute_call_cites_the_pages():

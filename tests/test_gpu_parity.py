@@ -503,6 +503,41 @@ def test_stack_graph_follows_rebuilt_layers():
     assert not torch.equal(ys[0], ys[1])
 
 
+# ------------------------------------------------------------------------ Q4_0 dequantisation
+
+def test_q4_dequant_bitwise_equals_oracle():
+    """The kernels' in-register Q4_0 unpacking, dumped by pi_q4_dequant, equals the oracle's
+    (q - 8) * s bit for bit (both exact): on quantised random rows with an all-zero block, a
+    block of equal magnitudes, extreme and subnormal scales, and on stored rows of an
+    OPT-175B-shaped layer (P1 «Kuantizasyon ve uyumluluk»)."""
+    from synth import quantize_q4_0
+    g = torch.Generator().manual_seed(5)
+    w = torch.randn((64, 1024), generator=g, dtype=torch.float32) * 0.05
+    w[0, :32] = 0.0                       # all-zero block: s = 0, q = 8
+    w[1, 32:64] = 0.25                    # every element at the absmax: codes clip to 15
+    w[2, 64:96] *= 1e4                    # large scale
+    w[3, 96:128] *= 1e-6                  # fp16-subnormal scale
+    codes, scales = quantize_q4_0(w)
+    sets = [(codes, scales)]
+    cfg = dataclasses.replace(CONFIGS["opt175b"], ffn=1024, rank=256)
+    L = make_layer(cfg, 0, device="cuda")
+    rows = torch.tensor([0, 1, 511, 1023])
+    sets.append((L.w_down_t.reshape(1024, -1, 16)[rows].cpu(), L.s_down[rows].cpu()))
+    sets.append((L.w_up.reshape(1024, -1, 16)[rows].cpu(), L.s_up[rows].cpu()))
+    ctx = make_ctx([L])
+    for c, sc in sets:
+        c = c.contiguous()
+        sc = sc.contiguous()
+        n, nb = sc.shape
+        out = torch.full((n, nb * 32), float("nan"), dtype=torch.float32, device="cuda")
+        pi.q4_dequant(ctx, c.cuda(), sc.view(torch.int16).cuda(), out)
+        torch.cuda.synchronize()
+        want = oracle.dequant_q4_0(c.numpy(), sc.numpy()).astype(np.float32)
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+            f"{int((got != want).sum())} of {got.size} dequantised weights differ"
+
+
 # ------------------------------------------------------------------------ permutation
 
 def test_hot_first_permutation_on_device():
