@@ -55,6 +55,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// a where the lane's mask m is all ones, b where it is zero, as bit operations on the
+// values. With plain `?:` selects over an array, the compiler turned the exchange steps below
+// into indexed reads of the whole array (a compare-and-select chain per value, or scratch):
+// about 1300 instructions for one 16-row reduction instead of about 100. (Written as inline
+// v_bfi_b32 instead, the instruction escaped the compiler's hazard checks after v_dot2c and
+// read a partly accumulated sum.)
+__device__ __forceinline__ float bfi_sel(uint32_t m, float a, float b) {
+  const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+  return __builtin_bit_cast(float, (ua & m) | (ub & ~m));
+}
+
 // Sum R per-lane partial rows over the 64 lanes of a wave with 2R-1+log2(64/R) shuffles:
 // each exchange step halves the rows a lane carries. On return every lane holds the full
 // sum of row (lane & (R-1)).
@@ -62,11 +73,11 @@ template <int R>
 __device__ __forceinline__ float transpose_reduce(float (&acc)[R], int lane) {
 #pragma unroll
   for (int o = R / 2; o >= 1; o >>= 1) {
-    const bool hi = (lane & o) != 0;
+    const uint32_t hi = (lane & o) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int i = 0; i < o; ++i) {
-      float send = hi ? acc[i] : acc[i + o];
-      float keep = hi ? acc[i + o] : acc[i];
+      const float send = bfi_sel(hi, acc[i], acc[i + o]);
+      const float keep = bfi_sel(hi, acc[i + o], acc[i]);
       acc[i] = keep + __shfl_xor(send, o, WAVE);
     }
   }
@@ -83,11 +94,11 @@ template <int R, int S>
 __device__ __forceinline__ float transpose_reduce_s(float (&acc)[R], int lane) {
 #pragma unroll
   for (int o = R / 2; o >= 1; o >>= 1) {
-    const bool hi = (lane & (o << S)) != 0;
+    const uint32_t hi = (lane & (o << S)) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int i = 0; i < o; ++i) {
-      float send = hi ? acc[i] : acc[i + o];
-      float keep = hi ? acc[i + o] : acc[i];
+      const float send = bfi_sel(hi, acc[i], acc[i + o]);
+      const float keep = bfi_sel(hi, acc[i + o], acc[i]);
       acc[i] = keep + __shfl_xor(send, o << S, WAVE);
     }
   }
