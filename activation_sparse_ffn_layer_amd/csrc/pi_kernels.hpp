@@ -1771,7 +1771,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (ii[u] < 0) continue;
+      // a missing item is skipped, except with quarter blocks, where its a * s is zero: there
+      // the skip put each pair's loads under a branch, so a round waited for all of them
+      if (!QPAIR && ii[u] < 0) continue;
       if constexpr (WT == W_F16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
