@@ -13,12 +13,15 @@
 //                                         mask words itself (no waiting on other workgroups),
 //                                         takes one group of active neurons over one column
 //                                         slice into a partial sum; the partials are added
-//                                         in a fixed order by k_reduce or the next layer's glue
+//                                         in a fixed order by k_reduce or the next layer's glue;
+//                                         k_down_q4x for Q4_0 rows at 4..8 tokens
 // Where the fused activations would make stage 2 slow (x of the batch above 64 KiB, Q4_0
-// rows, d >= 8192, 5..8 tokens), stage 2 stops after the threshold and k_up_cols (+ k_act_fin
-// when x is cut into several column slices) computes the activations instead.
+// rows, d >= 8192, 5..8 tokens), stage 2 stops after the threshold and k_up_cols or, for
+// Q4_0 rows, k_upq (+ k_act_fin when x is cut into several column slices) computes the
+// activations instead. At one token with chained layers, k_glue_sum adds the previous
+// layer's partial sums ahead of stage 1.
 // Plus k_up (the index-list entry point's gathered GEMV), k_compact, k_threshold, k_glue,
-// k_reduce and k_permute_rows.
+// k_reduce, k_q4_dequant and k_permute_rows.
 //
 // Pages: P3 = "PowerInfer: Mesin Inferensi LLM Cepat dengan GPU Konsumen" (unite.ai),
 // P1 = "Tüketici sınıfı GPU takılı PC'lerde yüksek hızlı büyük dil modeli serving".
@@ -1559,8 +1562,8 @@ __global__ __launch_bounds__(BLOCK) void k_act_fin(LayerDev L, int B, int S, con
 // tok_mask != nullptr (per-token masking, SCAN only): a[t][i] counts only where bit i of
 // token t's mask words tok_mask[t][ffn/64] is set; the scan keeps each listed neuron's token
 // bits next to it in LDS.
-// Q4_0 (QS lanes per 32-element block): QS = 1: a lane takes a whole block (16 code bytes);
-// QS = 4: a lane takes 4 code bytes, i.e. elements 4j..4j+3 and 16+4j..16+4j+3 of the block.
+// Q4_0 rows (1..2 tokens here; 4..8 take k_down_q4x): a lane takes a whole block (16 code
+// bytes, 32 columns), SQ lanes a slice.
 // ---------------------------------------------------------------------------------------
 // v of lane j of this lane's quad (DPP quad permutation; the quad's lanes must be active).
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int j) {
@@ -1573,73 +1576,47 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int j) {
   }
 }
 
-template <int WT, int QS, int SQ = 4 * QS> struct DownGeom {
-  static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32 / QS;  // columns per lane
+template <int WT, int SQ = 4> struct DownGeom {
+  static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32;  // columns per lane
   static constexpr int SEG = (WT == W_Q4) ? SQ : 8;                           // lanes per slice
   static constexpr int SW = SEG * EPC;                                         // slice width (columns)
 };
 
-// Column (within the slice) of element e of lane sl.
-template <int WT, int QS>
-__device__ __forceinline__ int down_col(int sl, int e) {
-  if constexpr (WT == W_Q4 && QS == 4) return (sl >> 2) * 32 + 4 * (sl & 3) + (e < 4 ? e : 12 + e);
-  else return sl * DownGeom<WT, QS>::EPC + e;
-}
-
 // Capacity of a group's neuron list (ints in LDS): every neuron of its words.
 __host__ __device__ constexpr int down_list_cap(int W, int G) { return (W + G - 1) / G * 64; }
 
-// Waves per SIMD the down kernel is held to: 3 at 8 tokens of Q4_0 rows (168 VGPRs instead of
-// 176; OPT-175B at 8 tokens 52.1 -> 45.9 us per layer on MI355X), else the compiler's choice.
-template <int WT, int NB> struct DownWaves { static constexpr int value = (WT == W_Q4 && NB >= 8) ? 3 : 1; };
-
-template <int WT, int NB, bool SCAN, int U, int QS, int G, int SQ = 4 * QS>
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves<WT, NB>::value))) void k_down_part(LayerDev L, int B, const uint64_t* __restrict__ words,
-                                                     const int32_t* __restrict__ idx_in,
-                                                     const int32_t* __restrict__ n_in, const float* __restrict__ a,
-                                                     const uint64_t* __restrict__ tok_mask,
-                                                     float* __restrict__ part, int32_t* __restrict__ idx_out,
-                                                     int32_t* __restrict__ n_out, int32_t* __restrict__ n_log) {
-  static_assert(G >= 1 && (G & (G - 1)) == 0, "the group count is a power of two");
-  constexpr int EPC = DownGeom<WT, QS, SQ>::EPC;
-  constexpr int SEG = DownGeom<WT, QS, SQ>::SEG;
-  constexpr int SW = SEG * EPC;
-  constexpr int NSL = BLOCK / SEG;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int red[NWAVES];
-  __shared__ int s_ng;
-  const int d = L.d, ffn = L.ffn, W = ffn >> 6;
-  int* il = reinterpret_cast<int*>(smem);  // the group's neurons [down_list_cap(W, G)]
-  // per-token masking: bit t of tb[j] = token t's mask bit of neuron il[j]
-  uint8_t* tb = reinterpret_cast<uint8_t*>(il + down_list_cap(W, G));
-  if constexpr (SCAN) {
-    if (blockIdx.x == 0) {  // the compaction block (dispatched first): ascending idx and n
-      uint64_t* wl = reinterpret_cast<uint64_t*>(smem);
-      int* pre = reinterpret_cast<int*>(wl + W);
-      const int n = scan_words(words, W, wl, pre, red);
-      for (int w = threadIdx.x; w < W; w += BLOCK) {
-        uint64_t word = wl[w];
-        int pos = pre[w];
-        while (word) {
-          idx_out[pos++] = w * WAVE + __ffsll((unsigned long long)word) - 1;
-          word &= word - 1;
-        }
-      }
-      if (threadIdx.x == 0) {
-        *n_out = n;
-        if (n_log != nullptr) *n_log = n;
-      }
-      return;
+// The compaction block of the down kernels: the ascending index list idx and its length n of
+// the union words (smem: the words, then their exclusive prefix counts).
+__device__ __forceinline__ void down_compact(const uint64_t* __restrict__ words, int W, uint8_t* smem, int* red,
+                                             int32_t* __restrict__ idx_out, int32_t* __restrict__ n_out,
+                                             int32_t* __restrict__ n_log) {
+  uint64_t* wl = reinterpret_cast<uint64_t*>(smem);
+  int* pre = reinterpret_cast<int*>(wl + W);
+  const int n = scan_words(words, W, wl, pre, red);
+  for (int w = threadIdx.x; w < W; w += BLOCK) {
+    uint64_t word = wl[w];
+    int pos = pre[w];
+    while (word) {
+      idx_out[pos++] = w * WAVE + __ffsll((unsigned long long)word) - 1;
+      word &= word - 1;
     }
   }
-  const int bid = SCAN ? (int)blockIdx.x - 1 : (int)blockIdx.x;  // SCAN: block 0 compacts
-  const int g = bid % G, s = bid / G;
-  const int slot = threadIdx.x / SEG, sl = threadIdx.x % SEG;
-  // the first column this lane touches; Q4 lanes of one block share a block index
-  const int col0 = s * SW + ((WT == W_Q4 && QS == 4) ? (sl >> 2) * 32 : sl * EPC);
-  const bool valid = col0 < d;
+  if (threadIdx.x == 0) {
+    *n_out = n;
+    if (n_log != nullptr) *n_log = n;
+  }
+}
+
+// Group g's neurons in ascending order into il (per-token masking: each one's token bits into
+// tb) and their count, which every thread gets back (a barrier inside).
+//  SCAN: from the union words w = g, g + G, ... (a block-wide pass per 256 words).
+//  else: the given list, filtered to the group's words, in list order.
+template <int NB, bool SCAN, int G>
+__device__ __forceinline__ int down_group_list(int g, int B, int W, int ffn, const uint64_t* __restrict__ words,
+                                               const int32_t* __restrict__ idx_in, const int32_t* __restrict__ n_in,
+                                               const uint64_t* __restrict__ tok_mask, int* il, uint8_t* tb, int* red,
+                                               int* s_ng) {
   if constexpr (SCAN) {
-    // the group's words in order (a block-wide pass per 256 words), their counts scanned
     const int nwg = (W - g + G - 1) / G;
     int carry = 0;
     for (int q0 = 0; q0 < nwg; q0 += BLOCK) {
@@ -1664,9 +1641,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
       }
       carry += total;
     }
-    if (threadIdx.x == 0) s_ng = carry;
+    if (threadIdx.x == 0) *s_ng = carry;
   } else {
-    // the given list, filtered to this group's words, in list order
     const int n = min(max(*n_in, 0), ffn);
     const int cap = down_list_cap(W, G);
     int carry = 0;
@@ -1679,10 +1655,197 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
       if (mine && carry + ex < cap) il[carry + ex] = i;
       carry += total;
     }
-    if (threadIdx.x == 0) s_ng = min(carry, cap);
+    if (threadIdx.x == 0) *s_ng = min(carry, cap);
   }
   __syncthreads();
-  const int ng = s_ng;
+  return *s_ng;
+}
+
+// Sum the NSL slots of each of the slice's SW columns in a fixed order and store the group's
+// partial part[g][t][col] for the B tokens. col_of(e) is the slice column of this lane's
+// element e. The slots' sums [NSL][SW + 1] take the LDS of the neuron list, which no thread
+// reads any more after the first barrier.
+template <int NB, int EPC, int SW, int NSL, class ColOf>
+__device__ __forceinline__ void down_store(uint8_t* smem, const float (&acc)[NB][EPC], ColOf col_of, int B, int g,
+                                           int s, int d, int slot, float* __restrict__ part) {
+  float (*s_red)[SW + 1] = reinterpret_cast<float (*)[SW + 1]>(smem);
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    if (t >= B) break;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) s_red[slot][col_of(e)] = acc[t][e];
+    __syncthreads();
+    for (int c = threadIdx.x; c < SW; c += BLOCK) {
+      const int col = s * SW + c;
+      if (col < d) {
+        float v = 0.f;
+        for (int q = 0; q < NSL; ++q) v += s_red[q][c];
+        part[((size_t)g * B + t) * d + col] = v;
+      }
+    }
+  }
+}
+
+// k_down_q4x: the down projection of Q4_0 rows at 4..8 tokens, with k_down_part's groups,
+// lists, compaction block and partial sums. A slice is 4 blocks (128 columns); the 4 lanes of
+// a block's quad take 4 code bytes each (elements 4j..4j+3 and 16+4j..16+4j+3 of the block)
+// and NB/4 of the tokens, whose a * s they form and share over the quad (DPP). Neurons are
+// taken two at a time: each column's two (q - 8) make an exact fp16 pair, multiplied by the
+// fp16 pair of the two a * s with dot2 (fp32 accumulation), one instruction per two weights
+// and token. Rounds of U list items per slot are software-pipelined: the loads of the next
+// round are issued before the products of this one. All loads are buffer loads: an item past
+// the list's end (or a slice past d) reads past its resource and gets zeros, so no load sits
+// under a branch.
+template <int NB, bool SCAN, int G, int U>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(NB >= 8 ? 3 : 1))) void k_down_q4x(
+    LayerDev L, int B, const uint64_t* __restrict__ words, const int32_t* __restrict__ idx_in,
+    const int32_t* __restrict__ n_in, const float* __restrict__ a, const uint64_t* __restrict__ tok_mask,
+    float* __restrict__ part, int32_t* __restrict__ idx_out, int32_t* __restrict__ n_out, int32_t* __restrict__ n_log) {
+  static_assert(NB == 4 || NB == 8, "4 or 8 tokens");
+  static_assert(U % 2 == 0, "items are taken in pairs");
+  static_assert(G >= 1 && (G & (G - 1)) == 0, "the group count is a power of two");
+  constexpr int SEG = 16, EPC = 8, SW = 128, NSL = BLOCK / SEG, TPL = NB / 4, R = NSL * U;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int red[NWAVES];
+  __shared__ int s_ng;
+  const int d = L.d, ffn = L.ffn, W = ffn >> 6, nbr = d >> 5;
+  int* il = reinterpret_cast<int*>(smem);
+  uint8_t* tb = reinterpret_cast<uint8_t*>(il + down_list_cap(W, G));
+  if constexpr (SCAN) {
+    if (blockIdx.x == 0) {  // the compaction block (dispatched first)
+      down_compact(words, W, smem, red, idx_out, n_out, n_log);
+      return;
+    }
+  }
+  const int bid = SCAN ? (int)blockIdx.x - 1 : (int)blockIdx.x;
+  const int g = bid % G, s = bid / G;
+  const int slot = threadIdx.x / SEG, sl = threadIdx.x % SEG, qd = sl & 3;
+  const int cb = s * (SW / 32) + (sl >> 2);  // this lane's block within a row
+  const bool valid = cb < nbr;
+  const int ng = down_group_list<NB, SCAN, G>(g, B, W, ffn, words, idx_in, n_in, tok_mask, il, tb, red, &s_ng);
+  const auto rw = buf_rsrc(L.w_down_t, (uint32_t)((size_t)ffn * nbr * 16));
+  const auto rs = buf_rsrc(L.s_down, (uint32_t)((size_t)ffn * nbr * 2));
+  const auto ra = buf_rsrc(a, (uint32_t)((size_t)ffn * NB * 4));
+  float acc[NB][EPC];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[t][e] = 0.f;
+  // one round's operands: code dword, scale bits, this lane's tokens' a, token bits
+  struct Round {
+    uint32_t c[U];
+    uint32_t sh[U];
+    uint32_t av[U][TPL];
+    uint32_t tbits[U];
+  };
+  auto load = [&](int j0, Round& r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + NSL * u;
+      const bool in = j < ng;
+      const uint32_t i = in ? (uint32_t)il[j] : 0u;
+      const uint32_t blk = i * (uint32_t)nbr + (uint32_t)cb;
+      const bool ok = in && valid;
+      r.c[u] = __builtin_amdgcn_raw_buffer_load_b32(rw, ok ? blk * 16u + qd * 4u : BUF_OOB, 0, 2);
+      r.sh[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? blk * 2u : BUF_OOB, 0, 0);
+      const uint32_t ao = in ? (i * NB + TPL * qd) * 4u : BUF_OOB;
+      if constexpr (TPL == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, ao, 0, 0);
+        r.av[u][0] = v[0];
+        r.av[u][1] = v[1];
+      } else {
+        r.av[u][0] = __builtin_amdgcn_raw_buffer_load_b32(ra, ao, 0, 0);
+      }
+      r.tbits[u] = (SCAN && tok_mask != nullptr && in) ? tb[j] : 0xFFu;
+    }
+  };
+  auto compute = [&](const Round& r) {
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      const uint32_t cu = r.c[u], cv = r.c[u + 1];
+      const uint32_t lu = cu & 0x0F0F0F0Fu, lv = cv & 0x0F0F0F0Fu;
+      const uint32_t hu = (cu >> 4) & 0x0F0F0F0Fu, hv = (cv >> 4) & 0x0F0F0F0Fu;
+      // byte k of u next to byte k of v: elements 4j+k (low nibbles), 16+4j+k (high)
+      const uint32_t l01 = __builtin_amdgcn_perm(lv, lu, 0x05010400u), l23 = __builtin_amdgcn_perm(lv, lu, 0x07030602u);
+      const uint32_t h01 = __builtin_amdgcn_perm(hv, hu, 0x05010400u), h23 = __builtin_amdgcn_perm(hv, hu, 0x07030602u);
+      uint32_t pr[8];
+      pr[0] = q4_pair(l01, SEL_B01);
+      pr[1] = q4_pair(l01, SEL_B23);
+      pr[2] = q4_pair(l23, SEL_B01);
+      pr[3] = q4_pair(l23, SEL_B23);
+      pr[4] = q4_pair(h01, SEL_B01);
+      pr[5] = q4_pair(h01, SEL_B23);
+      pr[6] = q4_pair(h23, SEL_B01);
+      pr[7] = q4_pair(h23, SEL_B23);
+      const float su = half_bits_to_float((uint16_t)r.sh[u]), sv = half_bits_to_float((uint16_t)r.sh[u + 1]);
+      // this lane's tokens' fp16 pairs of a * s (a token counts only where its bit is set and
+      // it is one of the B), then every token's pair from its quad lane
+      uint32_t pp[TPL];
+#pragma unroll
+      for (int h = 0; h < TPL; ++h) {
+        const int t = TPL * qd + h;
+        const float au = (t < B && ((r.tbits[u] >> t) & 1u)) ? u2f(r.av[u][h]) : 0.f;
+        const float bv = (t < B && ((r.tbits[u + 1] >> t) & 1u)) ? u2f(r.av[u + 1][h]) : 0.f;
+        pp[h] = __builtin_bit_cast(uint32_t, (half2_t){(half_t)(au * su), (half_t)(bv * sv)});
+      }
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const uint32_t ap = quad_bcast(pp[t % TPL], t / TPL);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = dot2(pr[e], ap, acc[t][e]);
+      }
+    }
+  };
+  // two rounds in flight: load the next while forming this one's products
+  Round r0, r1;
+  int j0 = slot;
+  load(j0, r0);
+  while (j0 < ng) {
+    load(j0 + R, r1);
+    compute(r0);
+    j0 += R;
+    if (j0 >= ng) break;
+    load(j0 + R, r0);
+    compute(r1);
+    j0 += R;
+  }
+  down_store<NB, EPC, SW, NSL>(smem, acc, [&](int e) { return (sl >> 2) * 32 + 4 * qd + (e < 4 ? e : 12 + e); },
+                               B, g, s, d, slot, part);
+}
+
+template <int WT, int NB, bool SCAN, int U, int G, int SQ = 4>
+__global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const uint64_t* __restrict__ words,
+                                                     const int32_t* __restrict__ idx_in,
+                                                     const int32_t* __restrict__ n_in, const float* __restrict__ a,
+                                                     const uint64_t* __restrict__ tok_mask,
+                                                     float* __restrict__ part, int32_t* __restrict__ idx_out,
+                                                     int32_t* __restrict__ n_out, int32_t* __restrict__ n_log) {
+  static_assert(G >= 1 && (G & (G - 1)) == 0, "the group count is a power of two");
+  static_assert(WT != W_Q4 || NB <= 2, "Q4_0 rows at 4..8 tokens take k_down_q4x");
+  constexpr int EPC = DownGeom<WT, SQ>::EPC;
+  constexpr int SEG = DownGeom<WT, SQ>::SEG;
+  constexpr int SW = SEG * EPC;
+  constexpr int NSL = BLOCK / SEG;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int red[NWAVES];
+  __shared__ int s_ng;
+  const int d = L.d, ffn = L.ffn, W = ffn >> 6;
+  int* il = reinterpret_cast<int*>(smem);  // the group's neurons [down_list_cap(W, G)]
+  // per-token masking: bit t of tb[j] = token t's mask bit of neuron il[j]
+  uint8_t* tb = reinterpret_cast<uint8_t*>(il + down_list_cap(W, G));
+  if constexpr (SCAN) {
+    if (blockIdx.x == 0) {  // the compaction block (dispatched first)
+      down_compact(words, W, smem, red, idx_out, n_out, n_log);
+      return;
+    }
+  }
+  const int bid = SCAN ? (int)blockIdx.x - 1 : (int)blockIdx.x;  // SCAN: block 0 compacts
+  const int g = bid % G, s = bid / G;
+  const int slot = threadIdx.x / SEG, sl = threadIdx.x % SEG;
+  const int col0 = s * SW + sl * EPC;  // the first column this lane touches
+  const bool valid = col0 < d;
+  const int ng = down_group_list<NB, SCAN, G>(g, B, W, ffn, words, idx_in, n_in, tok_mask, il, tb, red, &s_ng);
   float acc[NB][EPC];
   float qsum[NB];
 #pragma unroll
@@ -1705,43 +1868,28 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
       ii[u] = (j < ng) ? il[j] : -1;
       tbits[u] = (SCAN && tok_mask != nullptr && j < ng) ? tb[j] : 0xFFu;
     }
-    // activations first (small, likely cached; a neuron's NB tokens are contiguous), then the
-    // rows. With quarter blocks (QPAIR), each lane of a block's quad takes TPL = NB / 4 tokens
-    // and forms their a * s, which the quad's lanes then share.
-    constexpr bool QPAIR = WT == W_Q4 && QS == 4;
-    constexpr int TPL = QPAIR ? NB / 4 : NB;
-    const int qd = sl & 3;  // lane within the block's quad (QPAIR)
-    float av[U][TPL];
+    // activations first (small, likely cached; a neuron's NB tokens are contiguous), then the rows
+    float av[U][NB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float* ap = a + (size_t)(ii[u] >= 0 ? ii[u] : 0) * NB;
-      if constexpr (QPAIR) {
+      if constexpr (NB >= 4) {
 #pragma unroll
-        for (int h = 0; h < TPL; ++h) {
-          const int t = TPL * qd + h;
-          const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
-          const float v = ap[t];
-          av[u][h] = on ? v : 0.f;
+        for (int t4 = 0; t4 < NB; t4 += 4) {
+          const u32x4 v4 = ld16(ap + t4);  // zeroed below where ii[u] < 0
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[u][t4 + e] = u2f(v4[e]);
         }
       } else {
-        if constexpr (NB >= 4) {
 #pragma unroll
-          for (int t4 = 0; t4 < NB; t4 += 4) {
-            const u32x4 v4 = ld16(ap + t4);  // zeroed below where ii[u] < 0
+        for (int t = 0; t < NB; ++t) av[u][t] = ap[t];  // zeroed below where ii[u] < 0
+      }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) av[u][t4 + e] = u2f(v4[e]);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < NB; ++t) av[u][t] = ap[t];  // zeroed below where ii[u] < 0
-        }
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          // tokens past B hold no value; per-token masking: token t takes neuron i only if its
-          // own mask has it
-          const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
-          av[u][t] = on ? av[u][t] : 0.f;
-        }
+      for (int t = 0; t < NB; ++t) {
+        // tokens past B hold no value; per-token masking: token t takes neuron i only if its
+        // own mask has it
+        const bool on = ii[u] >= 0 && t < B && ((tbits[u] >> t) & 1u);
+        av[u][t] = on ? av[u][t] : 0.f;
       }
     }
     u32x4 w[U];
@@ -1758,12 +1906,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
         else if constexpr (WT == W_F32) w[u] = ld_stream_or0(L.w_down_t + (iu * d + cv) * 4, ok);
         else {
           const size_t blk = iu * (d >> 5) + (cv >> 5);
-          if constexpr (QS == 1) {
-            w[u] = ld_stream_or0(L.w_down_t + blk * 16, ok);
-          } else {
-            const uint32_t q = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(L.w_down_t + blk * 16) + (sl & 3));
-            w[u] = (u32x4){ok ? q : 0u, 0u, 0u, 0u};
-          }
+          w[u] = ld_stream_or0(L.w_down_t + blk * 16, ok);
           const float sv = half_bits_to_float(L.s_down[blk]);
           sc[u] = ok ? sv : 0.f;
         }
@@ -1771,9 +1914,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // a missing item is skipped, except with quarter blocks, where its a * s is zero: there
-      // the skip put each pair's loads under a branch, so a round waited for all of them
-      if (!QPAIR && ii[u] < 0) continue;
+      if (ii[u] < 0) continue;
       if constexpr (WT == W_F16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1789,7 +1930,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int t = 0; t < NB; ++t) acc[t][e] = fmaf(av[u][t], u2f(w[u][e]), acc[t][e]);
-      } else if constexpr (QS == 1) {
+      } else {
         float q[32];
         q4_block_codes(w[u], q);
 #pragma unroll
@@ -1798,39 +1939,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
           qsum[t] += as;
 #pragma unroll
           for (int e = 0; e < 32; ++e) acc[t][e] = fmaf(q[e], as, acc[t][e]);
-        }
-      } else if ((u & 1) == 0) {
-        // two neurons at a time (items u and u + 1; a missing one has a = 0): their (q - 8) of
-        // each column as an exact fp16 pair, times the fp16 pair of a * s per token with dot2
-        // (fp32 accumulation): one product instruction per two weights and token
-        static_assert(U % 2 == 0, "items are taken in pairs");
-        const uint32_t cu = w[u][0], cv = w[u + 1][0];
-        const uint32_t lu = cu & 0x0F0F0F0Fu, lv = cv & 0x0F0F0F0Fu;
-        const uint32_t hu = (cu >> 4) & 0x0F0F0F0Fu, hv = (cv >> 4) & 0x0F0F0F0Fu;
-        // byte k of u next to byte k of v: elements 4j+k (low nibbles), 16+4j+k (high)
-        const uint32_t l01 = __builtin_amdgcn_perm(lv, lu, 0x05010400u), l23 = __builtin_amdgcn_perm(lv, lu, 0x07030602u);
-        const uint32_t h01 = __builtin_amdgcn_perm(hv, hu, 0x05010400u), h23 = __builtin_amdgcn_perm(hv, hu, 0x07030602u);
-        uint32_t pr[8];
-        pr[0] = q4_pair(l01, SEL_B01);
-        pr[1] = q4_pair(l01, SEL_B23);
-        pr[2] = q4_pair(l23, SEL_B01);
-        pr[3] = q4_pair(l23, SEL_B23);
-        pr[4] = q4_pair(h01, SEL_B01);
-        pr[5] = q4_pair(h01, SEL_B23);
-        pr[6] = q4_pair(h23, SEL_B01);
-        pr[7] = q4_pair(h23, SEL_B23);
-        // this lane's tokens' fp16 pairs of a * s, then every token's from its quad lane
-        uint32_t pp[TPL];
-#pragma unroll
-        for (int h = 0; h < TPL; ++h) {
-          const half_t su = (half_t)(av[u][h] * sc[u]), sv = (half_t)(av[u + 1][h] * sc[u + 1]);
-          pp[h] = __builtin_bit_cast(uint32_t, (half2_t){su, sv});
-        }
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const uint32_t ap = quad_bcast(pp[t % TPL], t / TPL);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[t][e] = dot2(pr[e], ap, acc[t][e]);
         }
       }
     }
@@ -1841,26 +1949,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(DownWaves
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[t][e] = fmaf(-8.f, qsum[t], acc[t][e]);
   }
-  // sum the NSL slots of each column (fixed order) and store this group's partial; the slots'
-  // sums [NSL][SW + 1] take the LDS of the neuron list, which no thread reads any more after
-  // the first barrier below
-  float (*s_red)[SW + 1] = reinterpret_cast<float (*)[SW + 1]>(smem);
-#pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    if (t >= B) break;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) s_red[slot][down_col<WT, QS>(sl, e)] = acc[t][e];
-    __syncthreads();
-    for (int c = threadIdx.x; c < SW; c += BLOCK) {
-      const int col = s * SW + c;
-      if (col < d) {
-        float v = 0.f;
-        for (int q = 0; q < NSL; ++q) v += s_red[q][c];
-        part[((size_t)g * B + t) * d + col] = v;
-      }
-    }
-  }
+  down_store<NB, EPC, SW, NSL>(smem, acc, [&](int e) { return sl * EPC + e; }, B, g, s, d, slot, part);
 }
 
 // y[i] = sum_{g < G} part[g][i] over i < BD = B*d, groups summed in order (G <= 64). A

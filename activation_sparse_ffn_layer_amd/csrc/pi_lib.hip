@@ -488,6 +488,9 @@ pi_status launch_upq_t(pi_ctx* c, const LayerDev& L, const void* x, int B, int S
 // Slices and blocks per lane of k_upq for NB tokens; false where it does not apply.
 bool upq_geometry(const LayerDev& L, int NB, int* S, int* SB) {
   if (L.wtype != W_Q4) return false;
+  // its buffer loads address the rows with 32-bit offsets, and an offset of BUF_OOB must lie
+  // past them (larger rows take k_up_cols)
+  if ((size_t)L.ffn * (L.d / 32) * 16 >= BUF_OOB) return false;
   const int nbl = (L.d / 32 + WAVE - 1) / WAVE;  // blocks per lane over the whole row
   const int sb_max = (int)(UPQ_X_BUDGET / ((size_t)NB * 4 * WAVE * 16));
   const int s = (nbl + sb_max - 1) / sb_max;
@@ -551,22 +554,47 @@ constexpr int MM_KSD = 32;  // K splits of the batched down projection
 template <int WT, int NB, bool SCAN, int G, int SQ = 0, int UO = 0>
 pi_status launch_down_g(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
                         int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
-  constexpr int QS = (WT == W_Q4 && NB > 2) ? 4 : 1;
-  constexpr int SQE = SQ ? SQ : 4 * QS;
-  constexpr int U = UO ? UO : (WT == W_Q4) ? (QS == 4 ? 8 : (NB == 1 ? 8 : 4)) : (NB >= 4 ? 4 : 8);
+  constexpr int SQE = SQ ? SQ : 4;
+  constexpr int U = UO ? UO : (WT == W_Q4) ? (NB == 1 ? 8 : 4) : (NB >= 4 ? 4 : 8);
   const int W = L.ffn / 64;
   // the group's list (+ its per-token bits), then the slots' column sums; or the compaction
   // block's words and prefix
-  constexpr size_t lds_red = (size_t)(BLOCK / DownGeom<WT, QS, SQE>::SEG) * (DownGeom<WT, QS, SQE>::SW + 1) * 4;
+  constexpr size_t lds_red = (size_t)(BLOCK / DownGeom<WT, SQE>::SEG) * (DownGeom<WT, SQE>::SW + 1) * 4;
   const size_t lds = std::max({(size_t)down_list_cap(W, G) * 5, lds_red,
                                SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : (size_t)0});
   constexpr size_t lds_static = 256;
   if (lds + lds_static > c->lds_max)
     return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the down projection", L.ffn);
-  auto kern = k_down_part<WT, NB, SCAN, U, QS, G, SQE>;
+  auto kern = k_down_part<WT, NB, SCAN, U, G, SQE>;
   PI_HIP(c, allow_lds(kern, lds));
-  const int S = (L.d + DownGeom<WT, QS, SQE>::SW - 1) / DownGeom<WT, QS, SQE>::SW;
+  const int S = (L.d + DownGeom<WT, SQE>::SW - 1) / DownGeom<WT, SQE>::SW;
   // SCAN: one more block writes idx and n
+  PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a, tok_mask,
+                     c->part, idx_out, n_out, n_log));
+  c->down_g = G;
+  if (y != nullptr) {
+    const int BD = B * L.d;
+    PI_HIP(c, launch_k(c, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, c->part, G, BD, y));
+  }
+  return PI_OK;
+}
+
+// Q4_0 rows at 4..8 tokens: k_down_q4x, G groups, U list items per slot and round.
+template <int NB, bool SCAN, int G, int U>
+pi_status launch_down_q4x(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
+                          int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
+  // its buffer loads address the rows with 32-bit offsets, and an offset of BUF_OOB must lie
+  // past them
+  if ((size_t)L.ffn * (L.d / 32) * 16 >= BUF_OOB)
+    return fail(c, PI_ERR_UNSUPPORTED, "Q4_0 down rows of %d x %d exceed 2 GiB", L.ffn, L.d);
+  const int W = L.ffn / 64;
+  constexpr size_t lds_red = (size_t)(BLOCK / 16) * (128 + 1) * 4;
+  const size_t lds = std::max({(size_t)down_list_cap(W, G) * 5, lds_red,
+                               SCAN ? (size_t)W * 8 + (size_t)(W + 1) * 4 : (size_t)0});
+  if (lds + 256 > c->lds_max) return fail(c, PI_ERR_UNSUPPORTED, "ffn %d too large for the down projection", L.ffn);
+  auto kern = k_down_q4x<NB, SCAN, G, U>;
+  PI_HIP(c, allow_lds(kern, lds));
+  const int S = (L.d + 127) / 128;
   PI_HIP(c, launch_k(c, K_DOWN, kern, dim3(G * S + (SCAN ? 1 : 0)), lds, L, B, c->munion, idx_in, n_in, c->a, tok_mask,
                      c->part, idx_out, n_out, n_log));
   c->down_g = G;
@@ -598,9 +626,10 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   if constexpr (WT == W_Q4 && NB >= 4) {
     // 8 groups at 4..8 tokens of Q4_0 rows: one round of resident workgroups at the OPT-175B
     // shape (16 groups took two; 133 -> 128 us per layer at 8 tokens on MI355X)
-    return launch_down_g<WT, NB, SCAN, 8>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+    return launch_down_q4x<NB, SCAN, 8, 4>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+  } else {
+    return launch_down_g<WT, NB, SCAN, down_groups(NB)>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
   }
-  return launch_down_g<WT, NB, SCAN, down_groups(NB)>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
 }
 
 template <int WT, bool SCAN>
