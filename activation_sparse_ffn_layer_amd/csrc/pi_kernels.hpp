@@ -683,6 +683,62 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
 }
 
 // ---------------------------------------------------------------------------------------
+// k_stage1_x: z[t][j] = W1[j] . x_t for 2..8 tokens of given x (fp16, d <= 512 * PF). One
+// wave per row of W1 with the whole row in flight from entry (PF chunks of 16 bytes per
+// lane, chunk q of lane l = columns 8 (l + 64 q) .. + 7); x staged in LDS in column windows
+// of dc elements (d, or a multiple of 512), each window's chunks taken from registers once
+// the window is staged.
+// ---------------------------------------------------------------------------------------
+template <int NB, int PF>
+__global__ __launch_bounds__(BLOCK) void k_stage1_x(LayerDev L, const half_t* __restrict__ x, int B, int dc,
+                                                    float* __restrict__ z) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  half_t* xs = reinterpret_cast<half_t*>(smem);
+  const int d = L.d, r = L.rank, nch = d >> 3;
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int row = blockIdx.x * NWAVES + wave;
+  const uint8_t* wrow = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
+  u32x4 wv[PF];
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    const int c = lane + WAVE * q;
+    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
+  }
+  float acc[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[t] = 0.f;
+  for (int c0 = 0; c0 < d; c0 += dc) {
+    const int cw = min(dc, d - c0);
+    __syncthreads();
+    load_x_cols<NB, half_t>(x, B, d, c0, cw, xs, dc);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int c = lane + WAVE * q;  // chunk q's columns lie in this window, 512 q >= c0
+      if (WAVE * 8 * q >= c0 && WAVE * 8 * q < c0 + cw && c < nch) {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const u32x4 xv = ld16(xs + t * dc + (c * 8 - c0));
+          float s2 = acc[t];
+          s2 = dot2(wv[q][0], xv[0], s2);
+          s2 = dot2(wv[q][1], xv[1], s2);
+          s2 = dot2(wv[q][2], xv[2], s2);
+          s2 = dot2(wv[q][3], xv[3], s2);
+          acc[t] = s2;
+        }
+      }
+    }
+  }
+  if (row < r) {
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0 && t < B) z[(size_t)t * r + row] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // The glue between stacked layers at one token, in two steps, so that no workgroup of the
 // predictor reads the previous layer's G partial sums (G x d floats each).
 // k_glue_sum: workgroup s takes columns [4 * BLOCK * s, 4 * BLOCK * (s + 1)): y = the G
@@ -2024,6 +2080,88 @@ __global__ __launch_bounds__(BLOCK) void k_glue(const float* __restrict__ y, con
 #pragma unroll
         for (int e = 0; e < 4; ++e) xo[4 * c + e] = (XT)((u2f(v[j][e]) - u2f(cv[j][e])) / r);
     }
+  }
+}
+
+// k_glue_parts: the glue between stacked layers at 2..8 tokens, straight from the previous
+// layer's G partial sums: workgroup t (GLUE_NTH threads) adds token t's partials in group
+// order, u = y - c, and stores x = round(u / sqrt(mean(u^2))) (x_prev where y or u is all
+// zero). Each thread keeps its J chunks of 4 columns in registers between the sums of
+// squares and the store (d <= 4 * GLUE_NTH * J).
+constexpr int GLUE_NTH = 1024;
+template <int G, int J, bool XF32>
+__global__ __launch_bounds__(GLUE_NTH) void k_glue_parts(const float* __restrict__ part, int gstride,
+                                                         const float* __restrict__ center,
+                                                         const void* __restrict__ x_prev, int d,
+                                                         void* __restrict__ x_out) {
+  typedef typename XType<XF32>::T XT;
+  constexpr int NW = GLUE_NTH / WAVE;
+  // partials in flight per chunk: J * GU <= 16 loads of 16 bytes per thread at a time (more
+  // would not fit the 128 registers of a 1024-thread workgroup)
+  constexpr int GU = (J >= 3 ? 4 : 8) < G ? (J >= 3 ? 4 : 8) : G;
+  __shared__ float red[2 * NW];
+  const int t = blockIdx.x, n4 = d >> 2;
+  const float* pt = part + (size_t)t * d;
+  f32x4 u[J];
+  float ss = 0.f, su = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) u[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int g0 = 0; g0 < G; g0 += GU) {
+    u32x4 p[J][GU];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = threadIdx.x + GLUE_NTH * j;
+      const size_t off = 4 * (size_t)min(c, n4 - 1);
+#pragma unroll
+      for (int k = 0; k < GU; ++k) p[j][k] = ld16_or0(pt + (size_t)(g0 + k) * gstride + off, c < n4);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int k = 0; k < GU; ++k) u[j] += __builtin_bit_cast(f32x4, p[j][k]);
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = threadIdx.x + GLUE_NTH * j;
+    const u32x4 cv = center != nullptr ? ld16_or0(center + 4 * (size_t)min(c, n4 - 1), c < n4) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float yv = u[j][e];
+      u[j][e] = yv - u2f(cv[e]);
+      ss = fmaf(yv, yv, ss);
+      su = fmaf(u[j][e], u[j][e], su);
+    }
+  }
+  // block sums of both squares (fixed order)
+  ss = wave_sum(ss);
+  su = wave_sum(su);
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  if (lane == 0) {
+    red[w] = ss;
+    red[NW + w] = su;
+  }
+  __syncthreads();
+  ss = 0.f;
+  su = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    ss += red[i];
+    su += red[NW + i];
+  }
+  const float r = glue_divisor(ss, su, d);
+  const XT* xp = reinterpret_cast<const XT*>(x_prev) + (size_t)t * d;
+  XT* xo = reinterpret_cast<XT*>(x_out) + (size_t)t * d;
+  if (r == 0.f) {  // all-zero y or u: x passes through (r is the same in every thread)
+    for (int c = threadIdx.x; c < d; c += GLUE_NTH) xo[c] = xp[c];
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = threadIdx.x + GLUE_NTH * j;
+    if (c < n4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xo[4 * c + e] = (XT)(u[j][e] / r);
   }
 }
 

@@ -190,6 +190,27 @@ pi_status launch_stage1_nb(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) 
   return PI_OK;
 }
 
+// Stage 1 of 2..8 tokens of given x with the whole W1 row in flight from entry (d <= 512 PF).
+// Measured on MI355X against k_stage1 (same box): OPT-6.7B at 4 tokens 7.6 -> 6.4 us,
+// Llama-2-70B at 8 tokens 13.7 -> 13.1 us, OPT-175B at 8 tokens unchanged (19.5 us).
+template <int NB, int PF>
+pi_status launch_stage1_x_t(pi_ctx* c, const LayerDev& L, const void* x, int B) {
+  const int dc = x_window(c, NB, L.d, 2, X_LDS_BUDGET);
+  const size_t lds = (size_t)NB * dc * 2;
+  auto kern = k_stage1_x<NB, PF>;
+  PI_HIP(c, allow_lds(kern, lds));
+  const int grid = (L.rank + NWAVES - 1) / NWAVES;
+  PI_HIP(c, launch_k(c, K_STAGE1, kern, dim3(grid), lds, L, static_cast<const half_t*>(x), B, dc, c->z));
+  return PI_OK;
+}
+template <int NB>
+pi_status launch_stage1_x(pi_ctx* c, const LayerDev& L, const void* x, int B) {
+  if (L.d <= 512 * 8) return launch_stage1_x_t<NB, 8>(c, L, x, B);
+  if (L.d <= 512 * 16) return launch_stage1_x_t<NB, 16>(c, L, x, B);
+  if (L.d <= 512 * 24) return launch_stage1_x_t<NB, 24>(c, L, x, B);
+  return launch_stage1_x_t<NB, 32>(c, L, x, B);
+}
+
 // Stage 1 at one token that finishes the glue started by k_glue_sum (xin.ssq != nullptr).
 // The first 2/3 of the W1 row goes out at entry, behind u's loads; the rest once x is formed.
 // Measured on MI355X at the OPT-175B shape (d = 12288, 24 chunks per lane): 9.0 us with the
@@ -222,6 +243,33 @@ pi_status launch_glue_sum(pi_ctx* c, int d, const float* center, int* nsl) {
   return PI_OK;
 }
 
+// k_glue_parts over the previous layer's partial sums (2..8 tokens); glue_parts_ok says
+// where it applies (elsewhere k_reduce adds the partials and k_glue follows).
+template <int G, bool XF32>
+pi_status launch_glue_parts_g(pi_ctx* c, int B, int d, const float* center, const void* x_prev, void* x_out) {
+  const int J = (d / 4 + GLUE_NTH - 1) / GLUE_NTH;
+  const float* part = c->part;
+  const int gs = B * d;
+  switch (J) {
+    case 1: PI_HIP(c, launch_kb(c, K_REDUCE, k_glue_parts<G, 1, XF32>, dim3(B), GLUE_NTH, 0, part, gs, center, x_prev, d, x_out)); break;
+    case 2: PI_HIP(c, launch_kb(c, K_REDUCE, k_glue_parts<G, 2, XF32>, dim3(B), GLUE_NTH, 0, part, gs, center, x_prev, d, x_out)); break;
+    case 3: PI_HIP(c, launch_kb(c, K_REDUCE, k_glue_parts<G, 3, XF32>, dim3(B), GLUE_NTH, 0, part, gs, center, x_prev, d, x_out)); break;
+    default: PI_HIP(c, launch_kb(c, K_REDUCE, k_glue_parts<G, 4, XF32>, dim3(B), GLUE_NTH, 0, part, gs, center, x_prev, d, x_out));
+  }
+  return PI_OK;
+}
+bool glue_parts_ok(const pi_ctx* c, int d) {
+  return d % 4 == 0 && d <= 4 * GLUE_NTH * 4 && (c->down_g == 4 || c->down_g == 8 || c->down_g == 16);
+}
+template <bool XF32>
+pi_status launch_glue_parts(pi_ctx* c, int B, int d, const float* center, const void* x_prev, void* x_out) {
+  switch (c->down_g) {
+    case 4: return launch_glue_parts_g<4, XF32>(c, B, d, center, x_prev, x_out);
+    case 8: return launch_glue_parts_g<8, XF32>(c, B, d, center, x_prev, x_out);
+    default: return launch_glue_parts_g<16, XF32>(c, B, d, center, x_prev, x_out);
+  }
+}
+
 pi_status launch_stage1(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
   if (xin.ssq != nullptr) {
     if (B != 1 || !glue_split_ok(L.d, 2)) return fail(c, PI_ERR_INVALID, "split glue needs one token and d <= 16384");
@@ -229,6 +277,13 @@ pi_status launch_stage1(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) {
     if (L.d <= 512 * 16) return launch_stage1_g1_t<16>(c, L, xin);
     if (L.d <= 512 * 24) return launch_stage1_g1_t<24>(c, L, xin);
     return launch_stage1_g1_t<32>(c, L, xin);
+  }
+  if (xin.y == nullptr && B >= 2 && L.d <= 512 * 32 && L.d % 8 == 0) {
+    switch (nb_for(B)) {
+      case 2: return launch_stage1_x<2>(c, L, xin.x, B);
+      case 4: return launch_stage1_x<4>(c, L, xin.x, B);
+      default: return launch_stage1_x<8>(c, L, xin.x, B);
+    }
   }
   switch (nb_for(B)) {
     case 1: return launch_stage1_nb<1>(c, L, xin, B);
@@ -1373,15 +1428,24 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
           // several tokens: every predictor workgroup would re-read B x d partial sums, so the
           // partials are added and the glue applied once, by two small kernels
           const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-          const int BD = B * d;
-          PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part, ctx->down_g,
-                               BD, ctx->y));
-          if (xe == 4)
-            PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<true>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
-                                 ctx->xbuf[l & 1]));
-          else
-            PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
-                                 ctx->xbuf[l & 1]));
+          if (glue_parts_ok(ctx, d)) {
+            // one workgroup per token straight from the partials: one kernel of 7.6 us
+            // instead of k_reduce + k_glue (4.8 + 11.5 us) at the OPT-175B shape, 8 tokens,
+            // on MI355X (336 -> 344 tokens/s; OPT-6.7B at 4 tokens 1686 -> 1809 with stage 1
+            // above)
+            if (xe == 4) PI_TRY(launch_glue_parts<true>(ctx, B, d, center_into(l), x_prev, ctx->xbuf[l & 1]));
+            else PI_TRY(launch_glue_parts<false>(ctx, B, d, center_into(l), x_prev, ctx->xbuf[l & 1]));
+          } else {
+            const int BD = B * d;
+            PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_reduce, dim3((BD + WAVE - 1) / WAVE), 0, ctx->part, ctx->down_g,
+                                 BD, ctx->y));
+            if (xe == 4)
+              PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<true>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
+                                   ctx->xbuf[l & 1]));
+            else
+              PI_HIP(ctx, launch_k(ctx, K_REDUCE, k_glue<false>, dim3(B), 0, ctx->y, center_into(l), x_prev, d,
+                                   ctx->xbuf[l & 1]));
+          }
           xin = XIn{ctx->xbuf[l & 1], nullptr, nullptr, 1, 0, nullptr};
           x_cur = ctx->xbuf[l & 1];
         } else {
