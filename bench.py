@@ -132,18 +132,23 @@ def hot_prefix_auto(L, B):
     predicted-active probability Phi(mu / sqrt(1 + s2)). The prefix is the longest run from
     the hottest neuron over which the cumulative saving keeps growing."""
     import numpy as np
-    import scipy.special as sp
-    from synth import NOISE_VAR
     if L.rank <= 0:
         return 0
+    c = np.cumsum(hot_prefix_gain(L, B))
+    h = int(np.argmax(c)) + 1
+    return h if c[h - 1] > 0 else 0
+
+
+def hot_prefix_gain(L, B):
+    """Expected bytes a prefix saves per neuron, in stored (hot-first) order: its predictor row
+    (2r bytes) less its up (gate) and down rows, read even when it would not have fired."""
+    import scipy.special as sp
+    from synth import NOISE_VAR
     q = sp.ndtr(sp.ndtri(L.p) / math.sqrt(1.0 + NOISE_VAR))
     qb = 1.0 - (1.0 - q) ** B
     k = 3 if L.act == "reglu" else 2
     rows = k * L.d * WBYTES[L.wtype]
-    gain = 2.0 * L.rank - (1.0 - qb) * rows          # per neuron, in stored (hot-first) order
-    c = np.cumsum(gain)
-    h = int(np.argmax(c)) + 1
-    return h if c[h - 1] > 0 else 0
+    return 2.0 * L.rank - (1.0 - qb) * rows
 
 
 def build_stack(cfg, seed, pi, ctx, batch=1, mask_mode="union", hot_prefix="0"):
@@ -406,6 +411,9 @@ def main():
         "stream_read_gbs": round(stream_gbs, 1),
         "frac_of_stream_read": round(active_bytes / elapsed_s / 1e9 / stream_gbs, 4),
         "active_mb_per_step": round(active_bytes / args.steps / 1e6, 2),
+        # the bytes model's expected saving of the hot prefixes per step (hot-first layouts)
+        "hot_prefix_saved_mb_per_step": round(sum(float(hot_prefix_gain(L, B)[:L.hot_prefix].sum())
+                                                  for L in layers if getattr(L, "hot_prefix", 0) > 0) / 1e6, 3),
         "mean_active": round(float(nl.mean()) / cfg.ffn, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
