@@ -121,8 +121,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// Exclusive prefix sum of one int per thread over the block (BLOCK threads); returns the
-// thread's exclusive prefix and writes the block total to *total. `red` [NWAVES] ints in LDS.
+// Exclusive prefix sum of one int per thread over the block (NW waves, BLOCK threads by
+// default); returns the thread's exclusive prefix and writes the block total to *total.
+// `red` [NW] ints in LDS.
+template <int NW = NWAVES>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
   const int w = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   int incl = v;
@@ -136,7 +138,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < NWAVES; ++i) {
+  for (int i = 0; i < NW; ++i) {
     if (i < w) base += red[i];
     tot += red[i];
   }

@@ -1343,10 +1343,15 @@ __global__ __launch_bounds__(BLOCK) void k_up_cols(LayerDev L, const void* __res
 // per workgroup, each 16-byte piece of a block's 32 columns stored so that the 64 lanes of a
 // wave, taking consecutive blocks, read consecutive 16-byte words (no LDS bank conflicts):
 // piece m of local block b of token t sits at ((t * 4 + m) * 64 * SB + b) * 8 halves. The
-// neurons are dealt out without a prefix scan: from the union words, the workgroups of chunk
-// c take the 16-bit units c, c + NC, c + 2 NC, ... (unit u: bits 16 (u % 4) .. 16 (u % 4) + 15
-// of word u / 4), so the dense words of a hot-first layout spread over many workgroups; from
-// an index list, positions c, c + NC, ... Lane l takes blocks l, l + 64, ... of the slice (SB
+// neurons are dealt out from the union words: at 1..2 tokens without a prefix scan, the
+// workgroups of chunk c taking the 16-bit units c, c + NC, c + 2 NC, ... (unit u: bits
+// 16 (u % 4) .. 16 (u % 4) + 15 of word u / 4), so the dense words of a hot-first layout
+// spread over many workgroups; at 4..8 tokens evenly, every workgroup counting all the words
+// (a few KB, from L2) and the workgroups of chunk c taking the active neurons of rank
+// [c n / NC, (c + 1) n / NC), n the union's size, so that no workgroup needs a second round
+// of rows while others idle (measured on MI355X at the OPT-175B shape: 8 tokens 70.0 ->
+// 67.4 us; one token 13.7 -> 15.0 us, where the scan costs more than the balance saves).
+// From an index list, positions c, c + NC, ... Lane l takes blocks l, l + 64, ... of the slice (SB
 // of them); a wave takes RI neurons per round with every block of their rows in flight. Each
 // (row, token) partial is the lane's blocks ascending, then the wave sum: one per (row,
 // token) at 1..2 tokens, one transpose_reduce for all the round's sums at 4..8. With
@@ -1374,20 +1379,31 @@ __global__ __launch_bounds__(NTH) void k_upq(LayerDev L, const half_t* __restric
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);                                 // [NB][4][SLB][8]
   int* il = reinterpret_cast<int*>(smem + (size_t)NB * 4 * SLB * 16);           // [NTH]
+  uint64_t* wl = reinterpret_cast<uint64_t*>(il + NTH);                         // [W] union words
   __shared__ int wcnt[NW];
   const int d = L.d, ffn = L.ffn, W = ffn >> 6, nb = d >> 5;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int s = blockIdx.x, S = gridDim.x, ch = blockIdx.y, NC = gridDim.y;
   const int b0 = s * SLB;  // first block of the slice
-  // this thread's candidate neuron
+  constexpr bool BAL = NB >= 4;  // even shares of the union (else units of 16 bits)
+  // even shares: thread t counts the union words [t wpt, (t + 1) wpt)
+  const int wpt = (W + NTH - 1) / NTH, w0 = threadIdx.x * wpt;
+  int wc = 0;
+  if (BAL && words != nullptr)
+    for (int j = 0; j < wpt; ++j) {
+      const uint64_t word = (w0 + j < W) ? words[w0 + j] : 0ull;
+      if (w0 + j < W) wl[w0 + j] = word;
+      wc += __popcll(word);
+    }
+  // units of 16 bits, or the index list: this thread's candidate neuron
   int cand = -1;
-  if (words != nullptr) {
+  if (!BAL && words != nullptr) {
     const int k = threadIdx.x >> 4, u = ch + NC * k;
     const bool uok = k < upw && u < 4 * W;
     const uint64_t word = uok ? words[u >> 2] : 0ull;
     const int bit = 16 * (u & 3) + (threadIdx.x & 15);
     if (uok && ((word >> bit) & 1ull)) cand = (u >> 2) * WAVE + bit;
-  } else {
+  } else if (words == nullptr) {
     const int n = min(max(*n_in, 0), ffn);
     const int p = ch + NC * threadIdx.x;
     const int i = (p < n) ? idx_in[p] : -1;
@@ -1401,17 +1417,45 @@ __global__ __launch_bounds__(NTH) void k_upq(LayerDev L, const half_t* __restric
     const u32x4 v = ld16_or0(x + (size_t)min(t, B - 1) * d + (size_t)min(blk, nb - 1) * 32 + 8 * m, ok);
     *reinterpret_cast<u32x4*>(xs + (size_t)((t * 4 + m) * SLB + bl) * 8) = v;
   }
-  // candidates in thread order: ballot within the wave, wave counts through LDS
-  const uint64_t bal = __ballot(cand >= 0);
-  if (lane == 0) wcnt[wave] = __popcll(bal);
-  __syncthreads();
-  int base = 0, cnt = 0;
+  int cnt;
+  if (BAL && words != nullptr) {
+    // the union's ranks before this thread's words, and this workgroup's share of them
+    int n;
+    const int ex = block_exclusive_scan<NW>(wc, wcnt, &n);
+    const int lo = (int)((long long)ch * n / NC), hi = (int)((long long)(ch + 1) * n / NC);
+    cnt = hi - lo;  // <= ceil(ffn / NC) <= NTH (the launch's NC)
+    if (ex < hi && ex + wc > lo) {
+      int r = ex;
+      for (int j = 0; j < wpt; ++j) {
+        const int w = w0 + j;
+        if (w >= W || r >= hi) break;
+        uint64_t word = wl[w];
+        const int pc = __popcll(word);
+        if (r + pc <= lo) {
+          r += pc;
+          continue;
+        }
+        while (word) {
+          if (r >= lo && r < hi) il[r - lo] = w * WAVE + __ffsll((unsigned long long)word) - 1;
+          ++r;
+          word &= word - 1;
+        }
+      }
+    }
+  } else {
+    // candidates in thread order: ballot within the wave, wave counts through LDS
+    const uint64_t bal = __ballot(cand >= 0);
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int base = 0;
+    cnt = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    base += (w < wave) ? wcnt[w] : 0;
-    cnt += wcnt[w];
+    for (int w = 0; w < NW; ++w) {
+      base += (w < wave) ? wcnt[w] : 0;
+      cnt += wcnt[w];
+    }
+    if (cand >= 0) il[base + __popcll(bal & ((1ull << lane) - 1))] = cand;
   }
-  if (cand >= 0) il[base + __popcll(bal & ((1ull << lane) - 1))] = cand;
   __syncthreads();
   // the rows: codes and scales through bounds-checked buffer loads (a missing item or block
   // past d loads zeros without touching memory)

@@ -512,21 +512,22 @@ pi_status launch_upq_t(pi_ctx* c, const LayerDev& L, const void* x, int B, int S
   constexpr int NR = (ACT == ACT_REGLU) ? 2 : 1;
   if (S > 1 && (size_t)S * NR * B * L.ffn > c->hp_cap)
     return fail(c, PI_ERR_UNSUPPORTED, "layer %dx%d exceeds the context's slice buffer", L.d, L.ffn);
-  const int W = L.ffn / 64;
   // 16 waves, two neurons per wave and round. Measured on MI355X at the OPT-175B shape and 8
   // tokens: 86.6 us per layer; 12 waves with the next round's rows loading during this one's
   // arithmetic 88.5 us; 8 waves with 4 neurons per round (half the LDS reads of x), pipelined,
   // 102 us. The kernel is VALU- and LDS-bound there: about 180 VALU instructions per block and
   // row (16 dot2 per token), 57% VALU-busy.
   constexpr int NTH = 1024;
-  const size_t lds = (size_t)NB * 4 * WAVE * SB * 16 + (size_t)NTH * 4;
+  const size_t lds = (size_t)NB * 4 * WAVE * SB * 16 + (size_t)NTH * 4 + (size_t)(L.ffn / 64) * 8;
   auto kern = k_upq<ACT, NB, SB, 2, NTH>;
   PI_HIP(c, allow_lds(kern, lds));
   int per_cu = 0;
   PI_HIP(c, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NTH, lds));
   const int resident = std::max(1, per_cu) * c->cus;
+  // chunks of the neuron list: at most NTH candidates each, at least one workgroup per CU
+  const int W = L.ffn / 64;
   int nc, upw = 0;
-  if (words != nullptr) {
+  if (words != nullptr && NB <= 2) {
     nc = std::min(4 * W, std::max((4 * W + NTH / 16 - 1) / (NTH / 16), std::max(1, resident / S)));
     upw = (4 * W + nc - 1) / nc;
   } else {
@@ -541,7 +542,7 @@ pi_status launch_upq_t(pi_ctx* c, const LayerDev& L, const void* x, int B, int S
 }
 
 // Slices and blocks per lane of k_upq for NB tokens; false where it does not apply.
-bool upq_geometry(const LayerDev& L, int NB, int* S, int* SB) {
+bool upq_geometry(const pi_ctx* c, const LayerDev& L, int NB, int* S, int* SB) {
   if (L.wtype != W_Q4) return false;
   // its buffer loads address the rows with 32-bit offsets, and an offset of BUF_OOB must lie
   // past them (larger rows take k_up_cols)
@@ -553,7 +554,9 @@ bool upq_geometry(const LayerDev& L, int NB, int* S, int* SB) {
   if (sb > 6) return false;
   *S = s;
   *SB = sb <= 2 ? 2 : sb <= 3 ? 3 : 6;
-  return (size_t)NB * 4 * WAVE * *SB * 16 <= UPQ_X_BUDGET;
+  // x of the slice, the neuron list and the union words must fit the workgroup's LDS
+  return (size_t)NB * 4 * WAVE * *SB * 16 <= UPQ_X_BUDGET &&
+         UPQ_X_BUDGET + (size_t)UPQ_LIST * 4 + (size_t)(L.ffn / 64) * 8 <= c->lds_max;
 }
 
 template <int ACT, int NB>
@@ -581,7 +584,7 @@ pi_status launch_upq_a(pi_ctx* c, const LayerDev& L, const void* x, int B, int S
 pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, const uint64_t* words,
                          const int32_t* idx_in, const int32_t* n_in) {
   int S = 0, SB = 0;
-  if (B <= 8 && upq_geometry(L, nb_for(B), &S, &SB)) {
+  if (B <= 8 && upq_geometry(c, L, nb_for(B), &S, &SB)) {
     switch (L.act) {
       case ACT_RELU: return launch_upq_a<ACT_RELU>(c, L, x, B, S, SB, words, idx_in, n_in);
       case ACT_REGLU: return launch_upq_a<ACT_REGLU>(c, L, x, B, S, SB, words, idx_in, n_in);
