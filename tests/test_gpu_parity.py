@@ -428,11 +428,13 @@ def test_stack_predictor_graph_equals_eager_and_is_deterministic():
     check_layer(H0, X[:2].cpu().numpy(), out, TOL["f16"])
 
 
-@pytest.mark.parametrize("d,B", [(8192, 1), (8192, 2), (4096, 1)])
+@pytest.mark.parametrize("d,B", [(8192, 1), (8192, 2), (4096, 1), (4096, 4), (8192, 8), (12288, 3)])
 def test_stack_glue_of_partials_equals_layer_by_layer(d, B):
     """The stack hands each layer's down partial sums (4 groups for fp16 rows of 8192+ columns
-    at 1..2 tokens, else 8) to the next layer's glue. Chaining pi_layer and pi_glue by hand,
-    which sums them first, gives the same y up to rounding."""
+    at 1..2 tokens, 16 at 3..8 tokens, else 8) to the next layer's glue: at one token the
+    glue-sum kernel and stage 1, at 2..8 tokens one workgroup per token (1 to 3 chunks of
+    columns per thread). Chaining pi_layer and pi_glue by hand, which sums them first, gives
+    the same y up to rounding."""
     cfg = _cfg("falcon40b", layers=3, d=d, ffn=4096, rank=512)
     layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
     T = 2 * B
@@ -453,6 +455,32 @@ def test_stack_glue_of_partials_equals_layer_by_layer(d, B):
         for t in range(B):
             e = rel_l2(y_stack[s * B + t].cpu().numpy(), out["y"][t].cpu().numpy())
             assert e <= TOL["f16"], f"step {s} token {t}: rel L2 {e:.3e}"
+
+
+@pytest.mark.parametrize("B", [3, 8])
+def test_stack_glue_fp32_rows_equals_layer_by_layer(B):
+    """The same with fp32 rows and no predictor (true mask): the 2..8-token glue keeps x in
+    fp32."""
+    cfg = _cfg("tiny", layers=3, d=1536, ffn=2048)
+    layers = [make_layer(cfg, i, device="cuda") for i in range(cfg.layers)]
+    T = 2 * B
+    X = make_tokens(cfg, T, device="cuda", stream=6)
+    ctx = make_ctx(layers, max_batch=B)
+    ffns = [pi.Ffn(ctx, L) for L in layers]
+    y_stack = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    pi.stack_run(ctx, ffns, X, B, y_stack, None, use_graph=True)
+    for s in range(T // B):
+        x = X[s * B:(s + 1) * B].contiguous()
+        for li, f in enumerate(ffns):
+            out = run_layer(ctx, f, x)
+            if li + 1 < len(ffns):
+                xn = torch.empty_like(x)
+                pi.glue(ctx, out["y"], x, xn, layers[li].glue_center)
+                x = xn
+        torch.cuda.synchronize()
+        for t in range(B):
+            e = rel_l2(y_stack[s * B + t].cpu().numpy(), out["y"][t].cpu().numpy())
+            assert e <= TOL["f32"], f"step {s} token {t}: rel L2 {e:.3e}"
 
 
 @pytest.mark.parametrize("B", [1, 2])
