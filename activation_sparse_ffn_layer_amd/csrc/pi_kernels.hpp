@@ -1676,9 +1676,10 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int j) {
   }
 }
 
+// SQ: lanes per slice (Q4_0; fp16/fp32 rows take 8 unless SQ asks for more).
 template <int WT, int SQ = 4> struct DownGeom {
   static constexpr int EPC = (WT == W_F16) ? 8 : (WT == W_F32) ? 4 : 32;  // columns per lane
-  static constexpr int SEG = (WT == W_Q4) ? SQ : 8;                           // lanes per slice
+  static constexpr int SEG = (WT == W_Q4) ? SQ : (SQ > 8 ? SQ : 8);           // lanes per slice
   static constexpr int SW = SEG * EPC;                                         // slice width (columns)
 };
 

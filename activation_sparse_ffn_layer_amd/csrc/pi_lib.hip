@@ -604,7 +604,7 @@ pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, con
 // says how many there are.
 constexpr int DOWN_G = 8;        // partial sums (groups) at 1..2 tokens
 constexpr int DOWN_G_WIDE = 16;  // at 3..8 tokens, whose union lists are longer
-constexpr int DOWN_G_LONG = 4;   // at 1..2 tokens with fp16/fp32 rows of 8192 or more columns
+constexpr int DOWN_G_LONG = 8;   // at 1..2 tokens with fp16/fp32 rows of 8192 or more columns
 constexpr int down_groups(int NB) { return NB >= 4 ? DOWN_G_WIDE : DOWN_G; }
 constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
 constexpr int MM_KSD = 32;  // K splits of the batched down projection
@@ -663,10 +663,11 @@ pi_status launch_down_q4x(pi_ctx* c, const LayerDev& L, int B, const int32_t* id
   return PI_OK;
 }
 
-// Groups: fewer, longer lists at 1..2 tokens when fp16/fp32 rows have 8192+ columns (the
-// glue then adds 4 partial sums). Measured on MI355X against 8 groups: Falcon-40B and
-// Llama-2-70B at one token +2.5% and +2.9% tokens/s (down 18.1 -> 16.7 us, 17.3 -> 16.2 us);
-// Q4_0 rows (OPT-175B) lose 7.5% with 4 groups, OPT-6.7B (d = 4096) is unchanged.
+// fp16/fp32 rows of 8192+ columns at 1..2 tokens: 16 lanes (256 contiguous bytes of a row)
+// per neuron and slice, 8 groups. Measured on MI355X (same box) against 8 lanes and 4 groups:
+// Llama-2-70B down 16.3 -> 15.2-15.5 us per layer, Falcon-40B 16.4-16.9 -> 15.4-15.8 us
+// (16 lanes with 4 groups 18.6-19.6 us, 32 lanes with 8 groups 18.9-19.0 us); at OPT-6.7B
+// (d = 4096) 16 lanes were no faster, so it keeps 8 lanes and 8 groups.
 template <int WT, int NB, bool SCAN>
 pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_in, const int32_t* n_in, float* y,
                         int32_t* idx_out, int32_t* n_out, int32_t* n_log, const uint64_t* tok_mask) {
@@ -679,7 +680,7 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   }
   if constexpr (WT != W_Q4 && NB <= 2) {
     if (L.d >= 8192)
-      return launch_down_g<WT, NB, SCAN, DOWN_G_LONG>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+      return launch_down_g<WT, NB, SCAN, DOWN_G_LONG, 16>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
   }
   if constexpr (WT == W_Q4 && NB >= 4) {
     // 8 groups at 4..8 tokens of Q4_0 rows: one round of resident workgroups at the OPT-175B

@@ -430,8 +430,8 @@ def test_stack_predictor_graph_equals_eager_and_is_deterministic():
 
 @pytest.mark.parametrize("d,B", [(8192, 1), (8192, 2), (4096, 1), (4096, 4), (8192, 8), (12288, 3)])
 def test_stack_glue_of_partials_equals_layer_by_layer(d, B):
-    """The stack hands each layer's down partial sums (4 groups for fp16 rows of 8192+ columns
-    at 1..2 tokens, 16 at 3..8 tokens, else 8) to the next layer's glue: at one token the
+    """The stack hands each layer's down partial sums (8 groups at 1..2 tokens, 16 at 3..8
+    tokens) to the next layer's glue: at one token the
     glue-sum kernel and stage 1, at 2..8 tokens one workgroup per token (1 to 3 chunks of
     columns per thread). Chaining pi_layer and pi_glue by hand, which sums them first, gives
     the same y up to rounding."""
