@@ -549,23 +549,23 @@ __device__ __forceinline__ void act_rounds(const LayerDev& L, int B, int cnt, Id
 // Copy columns [c0, c0 + cw) of x [NB][d] (rows t >= B zeroed) into xs[t][0, cw) with
 // 16-byte accesses (cw * sizeof(XT) % 16 == 0). The NB x cw/E chunks form one flat range:
 // each thread issues J loads (over all tokens) before storing any.
-template <int NB, typename XT>
+template <int NB, typename XT, int NTH = BLOCK>
 __device__ __forceinline__ void load_x_cols(const void* x, int B, int d, int c0, int cw, XT* xs, int ldx) {
   constexpr int E = 16 / sizeof(XT);
-  constexpr int J = 16;
+  constexpr int J = 16 * BLOCK / NTH;
   const int n16 = cw / E, total = NB * n16;
-  for (int f0 = 0; f0 < total; f0 += BLOCK * J) {
+  for (int f0 = 0; f0 < total; f0 += NTH * J) {
     u32x4 v[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int f = f0 + threadIdx.x + BLOCK * j;
+      const int f = f0 + threadIdx.x + NTH * j;
       const int t = f / n16, c = f - t * n16;
       const bool ok = f < total && t < B;
       v[j] = ld16_or0(reinterpret_cast<const XT*>(x) + (ok ? (size_t)t * d + c * E : 0) + c0, ok);
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int f = f0 + threadIdx.x + BLOCK * j;
+      const int f = f0 + threadIdx.x + NTH * j;
       const int t = f / n16, c = f - t * n16;
       if (f < total) *reinterpret_cast<u32x4*>(xs + t * ldx + c * E) = v[j];
     }
@@ -683,26 +683,30 @@ __global__ __launch_bounds__(BLOCK) void k_stage1(LayerDev L, XIn xin, int B, in
 }
 
 // ---------------------------------------------------------------------------------------
-// k_stage1_x: z[t][j] = W1[j] . x_t for 2..8 tokens of given x (fp16, d <= 512 * PF). One
-// wave per row of W1 with the whole row in flight from entry (PF chunks of 16 bytes per
-// lane, chunk q of lane l = columns 8 (l + 64 q) .. + 7); x staged in LDS in column windows
-// of dc elements (d, or a multiple of 512), each window's chunks taken from registers once
-// the window is staged.
+// k_stage1_x: z[t][j] = W1[j] . x_t for 2..8 tokens of given x (fp16, d <= 512 * PF). KS
+// waves per row of W1, wave h of a row taking the chunk groups h, h + KS, ... (group g =
+// columns 512 g .. 512 g + 511, 16 bytes per lane), all of them in flight from entry; x
+// staged in LDS in column windows of dc elements (d, or a multiple of 512), each window's
+// chunks taken from registers once the window is staged. The KS shares of a row are added
+// in share order.
 // ---------------------------------------------------------------------------------------
-template <int NB, int PF>
-__global__ __launch_bounds__(BLOCK) void k_stage1_x(LayerDev L, const half_t* __restrict__ x, int B, int dc,
-                                                    float* __restrict__ z) {
+template <int NB, int PF, int KS>
+__global__ __launch_bounds__(BLOCK * KS) void k_stage1_x(LayerDev L, const half_t* __restrict__ x, int B, int dc,
+                                                         float* __restrict__ z) {
+  constexpr int NTH = BLOCK * KS, PFW = (PF + KS - 1) / KS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);
+  __shared__ float s_share[NWAVES * KS * NB];
   const int d = L.d, r = L.rank, nch = d >> 3;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int row = blockIdx.x * NWAVES + wave;
+  const int rw = wave / KS, h = wave % KS;  // row of the workgroup, share of the row
+  const int row = blockIdx.x * NWAVES + rw;
   const uint8_t* wrow = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
-  u32x4 wv[PF];
+  u32x4 wv[PFW];
 #pragma unroll
-  for (int q = 0; q < PF; ++q) {
-    const int c = lane + WAVE * q;
-    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
+  for (int q = 0; q < PFW; ++q) {
+    const int g = KS * q + h, c = lane + WAVE * g;
+    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && g < PF && c < nch);
   }
   float acc[NB];
 #pragma unroll
@@ -710,12 +714,12 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_x(LayerDev L, const half_t* __
   for (int c0 = 0; c0 < d; c0 += dc) {
     const int cw = min(dc, d - c0);
     __syncthreads();
-    load_x_cols<NB, half_t>(x, B, d, c0, cw, xs, dc);
+    load_x_cols<NB, half_t, NTH>(x, B, d, c0, cw, xs, dc);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int c = lane + WAVE * q;  // chunk q's columns lie in this window, 512 q >= c0
-      if (WAVE * 8 * q >= c0 && WAVE * 8 * q < c0 + cw && c < nch) {
+    for (int q = 0; q < PFW; ++q) {
+      const int g = KS * q + h, c = lane + WAVE * g;  // group g's columns lie in this window
+      if (g < PF && WAVE * 8 * g >= c0 && WAVE * 8 * g < c0 + cw && c < nch) {
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           const u32x4 xv = ld16(xs + t * dc + (c * 8 - c0));
@@ -729,12 +733,16 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_x(LayerDev L, const half_t* __
       }
     }
   }
-  if (row < r) {
 #pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const float s = wave_sum(acc[t]);
-      if (lane == 0 && t < B) z[(size_t)t * r + row] = s;
-    }
+  for (int t = 0; t < NB; ++t) {
+    const float s = wave_sum(acc[t]);
+    if (lane == 0) s_share[(rw * KS + h) * NB + t] = s;
+  }
+  __syncthreads();
+  if (h == 0 && lane < NB && lane < B && row < r) {
+    float v = 0.f;
+    for (int k = 0; k < KS; ++k) v += s_share[(rw * KS + k) * NB + lane];
+    z[(size_t)lane * r + row] = v;
   }
 }
 

@@ -197,10 +197,12 @@ template <int NB, int PF>
 pi_status launch_stage1_x_t(pi_ctx* c, const LayerDev& L, const void* x, int B) {
   const int dc = x_window(c, NB, L.d, 2, X_LDS_BUDGET);
   const size_t lds = (size_t)NB * dc * 2;
-  auto kern = k_stage1_x<NB, PF>;
+  constexpr int KS = 2;
+  auto kern = k_stage1_x<NB, PF, KS>;
   PI_HIP(c, allow_lds(kern, lds));
   const int grid = (L.rank + NWAVES - 1) / NWAVES;
-  PI_HIP(c, launch_k(c, K_STAGE1, kern, dim3(grid), lds, L, static_cast<const half_t*>(x), B, dc, c->z));
+  PI_HIP(c, launch_kb(c, K_STAGE1, kern, dim3(grid), BLOCK * KS, lds, L, static_cast<const half_t*>(x), B, dc,
+                      c->z));
   return PI_OK;
 }
 template <int NB>
