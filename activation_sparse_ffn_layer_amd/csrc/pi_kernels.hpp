@@ -753,9 +753,9 @@ __global__ __launch_bounds__(BLOCK * KS) void k_stage1_x(LayerDev L, const half_
 // partial sums added in group order (as glue_x adds them), u = y - c, stored to u[col]
 // (fp32), and the slice's sums of squares ssq[s] = {sum of y^2, sum of u^2}.
 // k_stage1_g1: adds the slices' sums in slice order, x = fp16(u / sqrt(mean(u^2))) (x_prev
-// when y or u is all zero), stores x to x_out (workgroup 0) and computes z = W1 x: one wave
-// per row of W1, the row's first PRE chunks issued at entry (behind the loads of u), the rest
-// once x is formed.
+// when y or u is all zero), stores x to x_out (workgroup 0) and computes z = W1 x: KS waves
+// per row of W1 (alternate 512-column chunk groups, their shares added in order), the row's
+// first PRE chunk groups issued at entry (behind the loads of u), the rest once x is formed.
 // ---------------------------------------------------------------------------------------
 constexpr int GLUE_SLICES_MAX = 16;  // slices of k_glue_sum: d <= 4 * BLOCK * 16
 
@@ -794,17 +794,22 @@ __global__ __launch_bounds__(BLOCK) void k_glue_sum(const float* __restrict__ pa
 
 // PF: chunks of 16 bytes per lane in a W1 row (d <= 512 * PF); u is read as PF / 2 chunks
 // of 4 floats per thread. PRE <= PF: chunks issued before x is formed.
-template <int PF, int PRE = PF>
-__global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __restrict__ u,
-                                                     const float* __restrict__ ssq, int nsl,
-                                                     const half_t* __restrict__ x_prev, half_t* __restrict__ x_out,
-                                                     float* __restrict__ z) {
-  constexpr int J = PF / 2;
+template <int PF, int PRE, int KS>
+__global__ __launch_bounds__(BLOCK * KS) void k_stage1_g1(LayerDev L, const float* __restrict__ u,
+                                                          const float* __restrict__ ssq, int nsl,
+                                                          const half_t* __restrict__ x_prev,
+                                                          half_t* __restrict__ x_out, float* __restrict__ z) {
+  constexpr int NTH = BLOCK * KS;
+  constexpr int J = (PF / 2 + KS - 1) / KS;     // chunks of 4 floats of u per thread
+  constexpr int PFW = (PF + KS - 1) / KS;       // chunk groups of the row per wave
+  constexpr int PREW = (PRE + KS - 1) / KS;     // of them issued before x is formed
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);
+  __shared__ float s_share[NWAVES * KS];
   const int d = L.d, r = L.rank;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int row = blockIdx.x * NWAVES + wave;
+  const int rw = wave / KS, h = wave % KS;  // row of the workgroup, share of the row
+  const int row = blockIdx.x * NWAVES + rw;
   const int n4 = d >> 2, nch = d >> 3;
   // the slices' sums of squares (the same addresses in every thread), then u, then the row
   u32x4 sq[GLUE_SLICES_MAX / 2];
@@ -814,16 +819,18 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
   u32x4 uv[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int c = threadIdx.x + BLOCK * j;
+    const int c = threadIdx.x + NTH * j;
     uv[j] = ld16_or0(u + 4 * (size_t)min(c, n4 - 1), c < n4);
   }
   const uint8_t* wrow = reinterpret_cast<const uint8_t*>(L.p_w1) + (size_t)min(row, r - 1) * d * 2;
-  u32x4 wv[PF];
+  // chunk group g = KS q + h of the row: columns 512 g .. 512 g + 511, 16 bytes per lane
+  u32x4 wv[PFW];
+  auto issue = [&](int q) {
+    const int g = KS * q + h, c = lane + WAVE * g;
+    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && g < PF && c < nch);
+  };
 #pragma unroll
-  for (int q = 0; q < PRE; ++q) {
-    const int c = lane + WAVE * q;
-    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
-  }
+  for (int q = 0; q < PREW; ++q) issue(q);
   float sy = 0.f, su = 0.f;
 #pragma unroll
   for (int k = 0; k < GLUE_SLICES_MAX / 2; ++k) {
@@ -842,7 +849,7 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
   if (rr != 0.f) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int c = threadIdx.x + BLOCK * j;
+      const int c = threadIdx.x + NTH * j;
       if (c < n4) {
         const half2_t h01 = {(half_t)(u2f(uv[j][0]) / rr), (half_t)(u2f(uv[j][1]) / rr)};
         const half2_t h23 = {(half_t)(u2f(uv[j][2]) / rr), (half_t)(u2f(uv[j][3]) / rr)};
@@ -852,7 +859,7 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
       }
     }
   } else {
-    for (int c = threadIdx.x; c < nch; c += BLOCK) {
+    for (int c = threadIdx.x; c < nch; c += NTH) {
       const u32x4 o = ld16(x_prev + 8 * c);
       *reinterpret_cast<u32x4*>(xs + 8 * c) = o;
       if (out) *reinterpret_cast<u32x4*>(x_out + 8 * c) = o;
@@ -860,17 +867,13 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
   }
   // the rest of the row after x
 #pragma unroll
-  for (int q = PRE; q < PF; ++q) {
-    const int c = lane + WAVE * q;
-    wv[q] = ld_stream_or0(wrow + (size_t)min(c, nch - 1) * 16, row < r && c < nch);
-  }
+  for (int q = PREW; q < PFW; ++q) issue(q);
   __syncthreads();
-  if (row >= r) return;
   float acc = 0.f;
 #pragma unroll
-  for (int q = 0; q < PF; ++q) {
-    const int c = lane + WAVE * q;
-    if (c < nch) {
+  for (int q = 0; q < PFW; ++q) {
+    const int g = KS * q + h, c = lane + WAVE * g;
+    if (g < PF && c < nch) {
       const u32x4 xv = ld16(xs + 8 * c);
       acc = dot2(wv[q][0], xv[0], acc);
       acc = dot2(wv[q][1], xv[1], acc);
@@ -879,7 +882,19 @@ __global__ __launch_bounds__(BLOCK) void k_stage1_g1(LayerDev L, const float* __
     }
   }
   acc = wave_sum(acc);
-  if (lane == 0) z[row] = acc;
+  if constexpr (KS == 1) {
+    if (lane == 0 && row < r) z[row] = acc;
+  } else {
+    // the row's shares, added in share order
+    if (lane == 0) s_share[rw * KS + h] = acc;
+    __syncthreads();
+    if (h == 0 && lane == 0 && row < r) {
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) v += s_share[rw * KS + k];
+      z[row] = v;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -220,11 +220,12 @@ pi_status launch_stage1_x(pi_ctx* c, const LayerDev& L, const void* x, int B) {
 template <int PF>
 pi_status launch_stage1_g1_t(pi_ctx* c, const LayerDev& L, const XIn& xin) {
   const size_t lds = (size_t)L.d * 2;
-  auto kern = k_stage1_g1<PF, PF * 2 / 3>;
+  constexpr int KS = 2;
+  auto kern = k_stage1_g1<PF, PF * 2 / 3, KS>;
   PI_HIP(c, allow_lds(kern, lds));
   const int grid = (L.rank + NWAVES - 1) / NWAVES;
-  PI_HIP(c, launch_k(c, K_STAGE1, kern, dim3(grid), lds, L, xin.y, xin.ssq, xin.nsl,
-                     static_cast<const half_t*>(xin.x), static_cast<half_t*>(xin.x_out), c->z));
+  PI_HIP(c, launch_kb(c, K_STAGE1, kern, dim3(grid), BLOCK * KS, lds, L, xin.y, xin.ssq, xin.nsl,
+                      static_cast<const half_t*>(xin.x), static_cast<half_t*>(xin.x_out), c->z));
   return PI_OK;
 }
 
