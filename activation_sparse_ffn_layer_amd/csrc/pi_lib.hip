@@ -238,7 +238,6 @@ pi_status launch_glue_sum(pi_ctx* c, int d, const float* center, int* nsl) {
   *nsl = (d / 4 + BLOCK - 1) / BLOCK;
   const dim3 grid(*nsl);
   switch (c->down_g) {
-    case 4: PI_HIP(c, launch_k(c, K_REDUCE, k_glue_sum<4>, grid, 0, c->part, d, center, d, c->y, c->ssq)); break;
     case 8: PI_HIP(c, launch_k(c, K_REDUCE, k_glue_sum<8>, grid, 0, c->part, d, center, d, c->y, c->ssq)); break;
     case 16: PI_HIP(c, launch_k(c, K_REDUCE, k_glue_sum<16>, grid, 0, c->part, d, center, d, c->y, c->ssq)); break;
     default: return fail(c, PI_ERR_UNSUPPORTED, "glue over %d partial sums", c->down_g);
@@ -262,12 +261,11 @@ pi_status launch_glue_parts_g(pi_ctx* c, int B, int d, const float* center, cons
   return PI_OK;
 }
 bool glue_parts_ok(const pi_ctx* c, int d) {
-  return d % 4 == 0 && d <= 4 * GLUE_NTH * 4 && (c->down_g == 4 || c->down_g == 8 || c->down_g == 16);
+  return d % 4 == 0 && d <= 4 * GLUE_NTH * 4 && (c->down_g == 8 || c->down_g == 16);
 }
 template <bool XF32>
 pi_status launch_glue_parts(pi_ctx* c, int B, int d, const float* center, const void* x_prev, void* x_out) {
   switch (c->down_g) {
-    case 4: return launch_glue_parts_g<4, XF32>(c, B, d, center, x_prev, x_out);
     case 8: return launch_glue_parts_g<8, XF32>(c, B, d, center, x_prev, x_out);
     default: return launch_glue_parts_g<16, XF32>(c, B, d, center, x_prev, x_out);
   }
@@ -607,7 +605,6 @@ pi_status launch_up_cols(pi_ctx* c, const LayerDev& L, const void* x, int B, con
 // says how many there are.
 constexpr int DOWN_G = 8;        // partial sums (groups) at 1..2 tokens
 constexpr int DOWN_G_WIDE = 16;  // at 3..8 tokens, whose union lists are longer
-constexpr int DOWN_G_LONG = 8;   // at 1..2 tokens with fp16/fp32 rows of 8192 or more columns
 constexpr int down_groups(int NB) { return NB >= 4 ? DOWN_G_WIDE : DOWN_G; }
 constexpr int MM_KS1 = 32;  // K splits of the batched predictor stage 1
 constexpr int MM_KSD = 32;  // K splits of the batched down projection
@@ -683,7 +680,7 @@ pi_status launch_down_t(pi_ctx* c, const LayerDev& L, int B, const int32_t* idx_
   }
   if constexpr (WT != W_Q4 && NB <= 2) {
     if (L.d >= 8192)
-      return launch_down_g<WT, NB, SCAN, DOWN_G_LONG, 16>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
+      return launch_down_g<WT, NB, SCAN, DOWN_G, 16>(c, L, B, idx_in, n_in, y, idx_out, n_out, n_log, tok_mask);
   }
   if constexpr (WT == W_Q4 && NB >= 4) {
     // 8 groups at 4..8 tokens of Q4_0 rows: one round of resident workgroups at the OPT-175B
@@ -1457,7 +1454,7 @@ static pi_status pi_stack_run_impl(pi_ctx* ctx, const pi_ffn* const* layers, int
           x_cur = ctx->xbuf[l & 1];
         } else {
           const void* x_prev = (l == 1) ? (const void*)ctx->xstage : (const void*)ctx->xbuf[(l - 1) & 1];
-          if (layers[l]->desc.rank > 0 && glue_split_ok(d, xe)) {
+          if (layers[l]->desc.rank > 0 && glue_split_ok(d, xe) && (ctx->down_g == 8 || ctx->down_g == 16)) {
             // the partial sums are added once (k_glue_sum); the predictor's stage 1 finishes
             // the glue from the centred sum and the slices' sums of squares
             int nsl = 0;
