@@ -910,8 +910,10 @@ __global__ __launch_bounds__(BLOCK * KS) void k_stage1_g1(LayerDev L, const floa
 // NB the batch class 1/2/4/8). x is staged in LDS while the W2 rows
 // are in flight (in column windows of width xw after the threshold when it does not fit).
 // ---------------------------------------------------------------------------------------
+// At 8 tokens without the activations the kernel is held to 4 waves per SIMD (124 instead of
+// 136 VGPRs): OPT-175B Q4_0 stage 2 31.3 -> 30.1 us per layer on MI355X.
 template <int NB, int CPL, bool UP, int WT, int ACT>
-__global__ __launch_bounds__(BLOCK) void k_stage2(LayerDev L, const float* __restrict__ z, int B,
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu((NB >= 8 && !UP) ? 4 : 1))) void k_stage2(LayerDev L, const float* __restrict__ z, int B,
                                                   uint64_t* __restrict__ mask_tok, uint64_t* __restrict__ mask_union,
                                                   float* __restrict__ logits, const void* __restrict__ x, int xw,
                                                   float* __restrict__ a) {
@@ -1980,8 +1982,9 @@ __global__ __launch_bounds__(BLOCK) void k_down_part(LayerDev L, int B, const ui
   }
   // Rounds of U list items per slot, all their row pieces in flight. At 4..8 tokens a missing
   // item (past the list's end) still issues its loads, from item 0's row, and drops them: with
-  // the loads under a branch the compiler waits for each one inside it (measured on MI355X:
-  // OPT-175B Q4_0 at 8 tokens, 77 -> 55 us per layer). At 1..2 tokens the branch is faster.
+  // the loads under a branch the compiler waits for each one inside it (measured on MI355X
+  // when this kernel still took Q4_0 rows at 8 tokens: OPT-175B 77 -> 55 us per layer). At
+  // 1..2 tokens the branch is faster.
   constexpr bool FULL = NB >= 4;
   for (int j0 = slot; j0 < ng; j0 += NSL * U) {
     int ii[U];

@@ -190,9 +190,11 @@ pi_status launch_stage1_nb(pi_ctx* c, const LayerDev& L, const XIn& xin, int B) 
   return PI_OK;
 }
 
-// Stage 1 of 2..8 tokens of given x with the whole W1 row in flight from entry (d <= 512 PF).
-// Measured on MI355X against k_stage1 (same box): OPT-6.7B at 4 tokens 7.6 -> 6.4 us,
-// Llama-2-70B at 8 tokens 13.7 -> 13.1 us, OPT-175B at 8 tokens unchanged (19.5 us).
+// Stage 1 of 2..8 tokens of given x (d <= 512 PF): two waves per W1 row, each with its whole
+// share in flight from entry. Measured on MI355X against k_stage1 (one wave per row, W1 in
+// windows): OPT-6.7B at 4 tokens 7.6 -> 5.6 us, Llama-2-70B at 8 tokens 13.7 -> 10.6 us,
+// OPT-175B at 8 tokens 19.3 -> 14.5 us; one wave per row with the whole row in flight left
+// OPT-175B at 19.5 us, and four waves per row were no better than two.
 template <int NB, int PF>
 pi_status launch_stage1_x_t(pi_ctx* c, const LayerDev& L, const void* x, int B) {
   const int dc = x_window(c, NB, L.d, 2, X_LDS_BUDGET);
@@ -213,9 +215,11 @@ pi_status launch_stage1_x(pi_ctx* c, const LayerDev& L, const void* x, int B) {
   return launch_stage1_x_t<NB, 32>(c, L, x, B);
 }
 
-// Stage 1 at one token that finishes the glue started by k_glue_sum (xin.ssq != nullptr).
-// The first 2/3 of the W1 row goes out at entry, behind u's loads; the rest once x is formed.
-// Measured on MI355X at the OPT-175B shape (d = 12288, 24 chunks per lane): 9.0 us with the
+// Stage 1 at one token that finishes the glue started by k_glue_sum (xin.ssq != nullptr), two
+// waves per W1 row (OPT-175B 8.4 -> 7.7 us per layer against one, Falcon-40B 6.2 -> 5.7,
+// Llama-2-70B 6.2 -> 5.4 on MI355X). The first 2/3 of each wave's share goes out at entry,
+// behind u's loads; the rest once x is formed. Measured with one wave per row at the OPT-175B
+// shape (d = 12288, 24 chunks per lane): 9.0 us with the
 // whole row issued at entry, 9.6 with none, 8.7 with 8 chunks, 8.2 with 16.
 template <int PF>
 pi_status launch_stage1_g1_t(pi_ctx* c, const LayerDev& L, const XIn& xin) {
