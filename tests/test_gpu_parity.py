@@ -125,6 +125,8 @@ CASES = {
     "q4-b7": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 3, 14, 7),
     "relu-b12-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 3, 24, 12),
     "reglu-b7-cols": (_cfg("llama70b", d=8192, ffn=4096, rank=512), 1, 7, 7),
+    # Q4_0 at 3 tokens (the 4-token kernels with a padded token) over a ragged last slice
+    "q4-b3-ragged": (_cfg("opt175b", d=800, ffn=640, rank=136), 0, 6, 3),
 }
 
 
@@ -184,6 +186,7 @@ PT_CASES = {
     "pt-sqrelu-b8": (_cfg("opt6.7b", act="sqrelu", d=1024, ffn=4096, rank=512), 1, 16, 8),
     "pt-reglu-b8-cols": (_cfg("llama70b", d=8192, ffn=4096, rank=512), 0, 8, 8),
     "pt-q4-b4": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 1, 8, 4),
+    "pt-q4-b8": (_cfg("opt175b", d=2048, ffn=8192, rank=512), 2, 16, 8),
     "pt-truemask-b8": (_cfg("llama70b", d=1024, ffn=4096, rank=None), 0, 8, 8),
     "pt-relu-b16-mfma": (_cfg("opt6.7b", d=1024, ffn=4096, rank=512), 2, 32, 16),
     "pt-reglu-b64-mfma": (_cfg("llama70b", d=1024, ffn=4096, rank=512), 2, 64, 64),
